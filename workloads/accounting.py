@@ -1,0 +1,77 @@
+"""Algorithmic work of a workload: FLOPs and HBM bytes the method itself
+needs, excluding padded or skipped work.
+
+Attention: QK^T and PV each cost 2*d FLOPs per legal (query, key) pair, the
+n^2 d term of the self-attention row of Table 1 (Deep-reading page section
+05).  Bytes: Q and O once, and only the legal K/V rows (padding rows need
+not be read), plus the int32 lengths.  GEMM: 2*M*N*K FLOPs and
+(M*K + K*N + M*N) elements.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .configs import MASK_CAUSAL, MASK_KEY_PADDING, Workload
+
+ELEM_BYTES = {"f32": 4, "bf16": 2}
+
+
+def legal_pairs(B, h, Lq, Lk, mask, kv_lens=None) -> int:
+    """Number of (b, head, i, j) with M_ij = 0."""
+    if mask & MASK_KEY_PADDING:
+        lens = np.clip(np.asarray(kv_lens, dtype=np.int64), 0, Lk)
+    else:
+        lens = np.full(B, Lk, dtype=np.int64)
+    total = 0
+    for L in lens:
+        L = int(L)
+        if mask & MASK_CAUSAL:
+            # query i sees keys 0..min(i, L-1): sum_i min(i+1, L)
+            m = min(L, Lq)
+            total += m * (m + 1) // 2 + (Lq - m) * L
+        else:
+            total += Lq * L
+    return total * h
+
+
+def attention_flops(B, h, Lq, Lk, d, mask, kv_lens=None) -> int:
+    return 4 * d * legal_pairs(B, h, Lq, Lk, mask, kv_lens)
+
+
+def attention_bytes(B, h, Lq, Lk, d, mask, kv_lens=None, dtype="bf16") -> int:
+    e = ELEM_BYTES[dtype]
+    if mask & MASK_KEY_PADDING:
+        kv_rows = int(np.clip(np.asarray(kv_lens, dtype=np.int64), 0, Lk).sum())
+    else:
+        kv_rows = B * Lk
+    qo = 2 * B * Lq * h * d
+    kv = 2 * kv_rows * h * d
+    lens = 4 * B if (mask & MASK_KEY_PADDING) else 0
+    return e * (qo + kv) + lens
+
+
+def gemm_flops(M, N, K) -> int:
+    return 2 * M * N * K
+
+
+def gemm_bytes(M, N, K, dtype="bf16") -> int:
+    return ELEM_BYTES[dtype] * (M * K + K * N + M * N)
+
+
+def workload_work(w: Workload, kv_lens=None) -> dict:
+    """Per-step algorithmic FLOPs and bytes of each stage of a workload."""
+    att_f = attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, kv_lens)
+    att_b = attention_bytes(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, kv_lens, w.dtype)
+    out = {"attention": {"flops": att_f, "bytes": att_b,
+                         "pairs": legal_pairs(w.B, w.h, w.Lq, w.Lk, w.mask, kv_lens)}}
+    if w.block:
+        M = w.B * w.Lq
+        n = w.h * w.d
+        qkv_f = 3 * gemm_flops(M, n, w.d_model)
+        # X read once (self-attention: X_q is X_kv), three weights, three outputs
+        qkv_b = ELEM_BYTES[w.dtype] * (M * w.d_model + 3 * w.d_model * n + 3 * M * n)
+        out["project_qkv"] = {"flops": qkv_f, "bytes": qkv_b}
+        out["out_proj"] = {"flops": gemm_flops(M, w.d_model, n),
+                           "bytes": gemm_bytes(M, w.d_model, n, w.dtype)}
+    out["total_flops"] = sum(v["flops"] for v in out.values() if isinstance(v, dict))
+    return out
