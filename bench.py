@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-head attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c3] [--gpus 1]
+
+One step is one pass of the whole hot path over one batch of seeded synthetic
+input: the Q/K/V projection, the fused masked attention and the W^O
+projection (the base decoder block by default: X [64, 128, 512], h = 8,
+d_k = 64, causal + key padding).  Each step is a replay of a HIP graph that
+holds the three launches; K steps run back to back, bracketed by
+torch.cuda.synchronize() and HIP events on the stream the kernels run on, and
+cycle over enough copies of every buffer that the 256 MB Infinity Cache
+cannot serve a repeat.
+
+Printed: one JSON line with the throughput (algorithmic TFLOP/s of the
+block), the roofline of the dominant kernel (timed alone with HIP events, in
+the same rotation), an attention-only sweep at L >= 1024 for the base and
+big head shapes, and the fp64 CPU oracle timed on the host as a reported
+baseline.
+
+Counter runs: ``--kernel-only NAME`` runs just one kernel (or a plain
+device copy of known size, ``copy``) so rocprofv3 --pmc can read its
+FETCH_SIZE / WRITE_SIZE.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+ROTATE_BYTES = 1 << 30        # rotate buffers over >= 1 GiB (Infinity Cache is 256 MB)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "attention": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc", "attention.hip"),
+    "project_qkv": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc", "gemm.hip"),
+    "out_proj": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc", "gemm.hip"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(name: str) -> str:
+    h = hashlib.sha256()
+    for p in sorted({KERNEL_SOURCES[name], os.path.join(os.path.dirname(KERNEL_SOURCES[name]),
+                                                       "device.h")}):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="rough CPU-time budget of the oracle sample")
+    ap.add_argument("--kernel-only", choices=["project_qkv", "attention", "out_proj", "copy"])
+    return ap.parse_args()
+
+
+class Block:
+    """Device buffers of one step of the block workload, in n_sets copies."""
+
+    def __init__(self, w, inputs, dev, n_sets):
+        import torch
+        import transformer_scaled_dot_fwd_amd as mha
+        self.w, self.mha = w, mha
+        B, L, h, d, dm = w.B, w.Lq, w.h, w.d, w.d_model
+        self.sets = []
+        for _ in range(n_sets):
+            s = {k: v.to(dev) if v is not None else None for k, v in inputs.items()}
+            s["q"] = torch.empty((B, L, h, d), dtype=torch.bfloat16, device=dev)
+            s["k"] = torch.empty_like(s["q"])
+            s["v"] = torch.empty_like(s["q"])
+            s["o"] = torch.empty_like(s["q"])
+            s["y"] = torch.empty((B, L, dm), dtype=torch.bfloat16, device=dev)
+            self.sets.append(s)
+
+    def project_qkv(self, s):
+        self.mha.mha_project_qkv(s["x"], s["x"], s["w_q"], s["w_k"], s["w_v"], self.w.h,
+                                 out=(s["q"], s["k"], s["v"]))
+
+    def attention(self, s):
+        self.mha.mha_forward(s["q"], s["k"], s["v"], mask=self.w.mask, kv_lens=s["kv_lens"],
+                             out=s["o"])
+
+    def out_proj(self, s):
+        self.mha.mha_out_proj(s["o"], s["w_o"], out=s["y"])
+
+    def step(self, s):
+        self.project_qkv(s)
+        self.attention(s)
+        self.out_proj(s)
+
+
+def working_set_bytes(tensors) -> int:
+    return sum(t.numel() * t.element_size() for t in tensors if t is not None)
+
+
+def capture(fn_per_set, sets):
+    """One HIP graph per buffer set, each holding fn(set)."""
+    import torch
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the launch path outside capture
+        for s in sets:
+            fn_per_set(s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for s in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn_per_set(s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graphs(graphs, n, warmup):
+    """Replay graphs[i % len] for i < n; return seconds per replay."""
+    import torch
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        graphs[i % len(graphs)].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / n
+
+
+def kernel_time(fn, sets, launches, warmup):
+    """Average duration of one launch of fn, timed in graphs that each hold
+    one launch per buffer set (so consecutive launches use different
+    buffers)."""
+    g = capture(lambda s0: [fn(s) for s in sets], sets[:1])
+    reps = max(1, math.ceil(launches / len(sets)))
+    return time_graphs(g, reps, max(1, warmup // len(sets))) / len(sets)
+
+
+def traffic_for(name, launches_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when absent or taken on a different version of the kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(name)
+    if not e or e.get("source_sha") != source_sha(name) or e.get("workload") != launches_key:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def attention_sweep(dev, steps, warmup):
+    """Attention alone at the base (h=8) and big (h=16) shapes, L >= 1024,
+    plus the long causal workload."""
+    import torch
+    import transformer_scaled_dot_fwd_amd as mha
+    from workloads import accounting, configs
+    out = []
+    for w in [configs.get("c5")] + configs.sweep():
+        inp = configs.make_inputs(w)
+        one = working_set_bytes([inp["q"], inp["k"], inp["v"], inp["q"]])
+        n_sets = max(2, min(16, math.ceil(ROTATE_BYTES / one)))
+        sets = []
+        for _ in range(n_sets):
+            s = {k: v.to(dev) if v is not None else None for k, v in inp.items()}
+            s["o"] = torch.empty_like(s["q"])
+            sets.append(s)
+        fn = lambda s: mha.mha_forward(s["q"], s["k"], s["v"], mask=w.mask,
+                                       kv_lens=s["kv_lens"], out=s["o"])
+        sec = kernel_time(fn, sets, max(steps // 4, 2 * n_sets), warmup)
+        flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, inp["kv_lens"])
+        tf = flops / sec / 1e12
+        out.append({"workload": w.name, "B": w.B, "h": w.h, "L": w.Lq,
+                    "mask": "causal" if w.mask & 2 else "none", "us": round(sec * 1e6, 2),
+                    "tflops": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)})
+        log(f"  sweep {w.name}: {sec * 1e6:.1f} us, {tf:.1f} TFLOP/s "
+            f"({100 * tf * 1e12 / PEAK_BF16_FLOPS:.1f}% of bf16 peak)")
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w, inputs, budget_s, flops_per_step):
+    """The fp64 oracle (as it stands) on a bounded sample of the same
+    workload: whole batch rows of the block, sized to roughly budget_s."""
+    import oracle
+    from workloads import accounting
+    x, ws = inputs["x"], [inputs[k] for k in ("w_q", "w_k", "w_v", "w_o")]
+    lens = inputs["kv_lens"]
+
+    def run(nb):
+        t0 = time.perf_counter()
+        oracle.mha_block(x[:nb], x[:nb], *ws, h=w.h, mask=w.mask,
+                         kv_lens=None if lens is None else lens[:nb])
+        return time.perf_counter() - t0
+
+    def flops(nb):
+        sub = accounting.workload_work(dataclasses.replace(w, B=nb),
+                                       None if lens is None else lens[:nb].numpy())
+        return sub["total_flops"]
+
+    probe = run(1)
+    nb = int(max(1, min(w.B, budget_s / max(probe, 1e-3))))
+    sec = run(nb)
+    rate = flops(nb) / sec
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{nb} of {w.B} batch rows of the block (projection, attention, W^O), "
+                      f"one run, {sec:.2f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_scaled_dot_fwd_amd as mha
+    from workloads import accounting, configs
+
+    mha.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = configs.get(args.workload)
+    if not w.block:
+        raise SystemExit("the benchmark step is the full block: pick a block workload (c3)")
+    inputs = configs.make_inputs(w)
+    work = accounting.workload_work(w, inputs["kv_lens"].numpy()
+                                    if inputs["kv_lens"] is not None else None)
+
+    probe = Block(w, inputs, dev, 1)
+    s0 = probe.sets[0]
+    one = working_set_bytes([s0[k] for k in ("x", "w_q", "w_k", "w_v", "w_o", "q", "k", "v",
+                                             "o", "y")])
+    n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / one)))
+    del probe
+    blk = Block(w, inputs, dev, n_sets)
+    log(f"workload {w.name}: working set {one / 1e6:.1f} MB x {n_sets} rotating sets")
+
+    if args.kernel_only:
+        fns = {"project_qkv": blk.project_qkv, "attention": blk.attention,
+               "out_proj": blk.out_proj}
+        if args.kernel_only == "copy":
+            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(args.steps):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log("copy: 256 MiB per launch")
+        else:
+            for i in range(args.steps):
+                fns[args.kernel_only](blk.sets[i % n_sets])
+            torch.cuda.synchronize()
+            log(f"{args.kernel_only}: {args.steps} launches")
+        return
+
+    # ---- whole step: K graph replays, each one step on its own buffer set ----
+    graphs = capture(blk.step, blk.sets)
+    sec_step = time_graphs(graphs, args.steps, args.warmup)
+    flops_step = work["total_flops"]
+    value = flops_step / sec_step / 1e12
+    log(f"step: {sec_step * 1e6:.2f} us, {value:.1f} TFLOP/s")
+
+    # ---- per-kernel durations, each timed alone in the same rotation ----
+    per = {}
+    for name in ("project_qkv", "attention", "out_proj"):
+        fn = getattr(blk, name)
+        per[name] = kernel_time(fn, blk.sets, max(args.steps, 2 * n_sets), args.warmup)
+        log(f"  {name}: {per[name] * 1e6:.2f} us")
+    dom = max(per, key=per.get)
+    if dom == "attention":
+        bound, alg, unit, peak = "hbm", work["attention"]["bytes"], "GB/s", PEAK_HBM_BYTES
+    else:
+        bound, alg, unit, peak = "mfma", work[dom]["flops"], "TFLOP/s", PEAK_BF16_FLOPS
+    achieved = alg / per[dom]
+    scale = 1e9 if unit == "GB/s" else 1e12
+    traffic = traffic_for(dom, w.name)
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved / scale, 2),
+                "peak": round(peak / scale, 1), "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "avg_launch_us": round(per[dom] * 1e6, 3)}
+    kernels = {}
+    for name, sec in per.items():
+        f = work[name]["flops"]
+        b = work[name]["bytes"]
+        kernels[name] = {"us": round(sec * 1e6, 3), "tflops": round(f / sec / 1e12, 1),
+                         "gbps": round(b / sec / 1e9, 1)}
+
+    sweep = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inputs, args.cpu_seconds, flops_step)
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": "attention fwd TFLOP/s & % peak bf16 MFMA at h=8,d_k=64 (1 MI355X)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,1/512) weights, lengths U{32..128})",
+        "config": {"workload": w.name, "B": w.B, "L": w.Lq, "d_model": w.d_model, "h": w.h,
+                   "d_k": w.d, "mask": "causal+key_padding", "step": "project_qkv -> "
+                   "attention -> out_proj (HIP graph replay)", "rotating_sets": n_sets,
+                   "flops_per_step": flops_step},
+        "frac_peak_bf16": round(value * 1e12 / PEAK_BF16_FLOPS, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "attention_sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

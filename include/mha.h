@@ -1,0 +1,145 @@
+/*
+ * mha.h -- C ABI of the MI355X (gfx950) multi-head scaled dot-product
+ * attention forward library, libmha.so.
+ *
+ * The operations are those of "Attention Is All You Need" as stated on the
+ * pages this library follows:
+ *   [Slides]     "Attention Is All You Need -- A Revolutionary Architecture
+ *                for Sequence Transduction" (slide deck)
+ *   [Deep]       "Paper Deep Reading: Attention Is All You Need"
+ *   [Paperglide] "Attention Is All You Need" explainer (paperglide)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *   row-major, 16-byte aligned.  The library never allocates, frees or
+ *   synchronises; it keeps no state besides a cached device-property query,
+ *   and is safe to call from several host threads.
+ * - All work is enqueued on `stream` (a hipStream_t; NULL means the legacy
+ *   default stream) and runs asynchronously: a return of MHA_OK means the
+ *   arguments were accepted and the kernels launched, not that they finished.
+ * - Every tensor of one call has the element type `dt`; arithmetic
+ *   accumulates in fp32 and stores round to nearest even.
+ * - "BLHD" is the layout [B, L, h, d] (row-major).  It is byte-identical to
+ *   the [B*L, h*d] matrix X W with head t in column block t, and to
+ *   Concat(head_1, ..., head_h) ([Paperglide] two-head toy example; [Deep]
+ *   section 04, MultiHead equations).
+ * - Errors: the return value is an mha_status.  Arguments are validated on
+ *   the host before any HIP call; a rejected call launches nothing and
+ *   leaves every buffer untouched.  MHA_ERR_LAUNCH reports a failed kernel
+ *   launch (hipGetLastError after the launch).
+ */
+#ifndef MHA_H
+#define MHA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MHA_OK = 0,
+    MHA_ERR_INVALID_ARG = 1, /* a dimension < 1 (or < 0 where 0 is allowed),
+                                a NULL pointer, KEY_PADDING without kv_lens,
+                                CAUSAL with Lq != Lk, an unknown dtype/mask */
+    MHA_ERR_UNSUPPORTED = 2, /* valid but not compiled: d_k != d_v, a head
+                                size or GEMM width outside the built set */
+    MHA_ERR_LAUNCH = 3       /* the kernel launch failed */
+} mha_status;
+
+typedef enum { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype;
+
+/* Mask bit flags for M; MHA_MASK_KEY_PADDING | MHA_MASK_CAUSAL is their
+ * union (-inf wherever either applies). */
+enum {
+    MHA_MASK_NONE = 0,
+    MHA_MASK_KEY_PADDING = 1, /* key j of batch row b is illegal iff
+                                 j >= clamp(kv_lens[b], 0, Lk); the encoder
+                                 masks padding ([Deep] section 04) */
+    MHA_MASK_CAUSAL = 2       /* key j is illegal for query i iff j > i; the
+                                 decoder also masks future positions
+                                 ([Deep] section 03 "Decoder layer" and
+                                 section 04); requires Lq == Lk */
+};
+
+/*
+ * mha_forward -- scaled dot-product attention for every (batch row, head):
+ *
+ *     O = softmax(Q K^T / sqrt(d_k) + M) V
+ *
+ * ([Deep] section 04, attention equation with M; [Slides] slide "Attention
+ * Mechanism").  M is 0 at legal (query, key) pairs and -inf at illegal ones
+ * (mask_flags above); the weights of illegal keys are exactly 0.
+ *
+ *   q  [B, Lq, h, d_k]  BLHD   queries (for cross-attention: decoder side)
+ *   k  [B, Lk, h, d_k]  BLHD   keys    (for cross-attention: encoder memory)
+ *   v  [B, Lk, h, d_v]  BLHD   values
+ *   o  [B, Lq, h, d_v]  BLHD   output, written in full (this IS the concat
+ *                              of the heads); must not overlap q, k or v
+ *   kv_lens  int32 [B] on the device: valid key count per batch row,
+ *            required iff MHA_MASK_KEY_PADDING is set, else ignored (may be
+ *            NULL); values outside [0, Lk] are clamped.
+ *
+ * Rows of K and V at or beyond kv_lens[b] are never read and may hold any
+ * bits (NaN included).  Rows below kv_lens[b] must be finite.  A query row
+ * with no legal key (kv_lens[b] == 0) outputs exactly 0.  Padded query rows
+ * are computed like any other row.
+ *
+ * Supported: B, h, Lq, Lk >= 1 (B*h*ceil(Lq/128) < 2^31), d_k == d_v;
+ * MHA_BF16 with d_k = 64; MHA_F32 with d_k in {8, 16, 32, 64}.
+ */
+int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v,
+                const void* q, const void* k, const void* v,
+                int mask_flags, const int32_t* kv_lens,
+                void* o, hipStream_t stream);
+
+/*
+ * mha_project_qkv -- the per-head projections of every head at once:
+ *
+ *     Q = X_q W^Q,  K = X_kv W^K,  V = X_kv W^V
+ *
+ * with W^Q = [W_1^Q || ... || W_h^Q] etc., so head t of Q is column block t
+ * ([Slides] slide "Multi-Head Attention": head_i = Attention(Q W_i^Q,
+ * K W_i^K, V W_i^V); [Paperglide] two-head toy example).  No bias.
+ *
+ *   x_q   [B, Lq, d_model]           decoder (or self-attention) input
+ *   x_kv  [B, Lk, d_model]           key/value source: the same pointer as
+ *                                    x_q for self-attention, the encoder
+ *                                    memory z for cross-attention
+ *   w_q, w_k  [d_model, h*d_k]       row-vector convention: out = x W
+ *   w_v       [d_model, h*d_v]
+ *   q  [B, Lq, h, d_k], k [B, Lk, h, d_k], v [B, Lk, h, d_v]  BLHD outputs;
+ *   outputs must not overlap the inputs or each other.
+ *
+ * Supported: MHA_BF16 and MHA_F32; d_model % 64 == 0, h*d_k % 64 == 0,
+ * d_k == d_v.
+ */
+int mha_project_qkv(mha_dtype dt, int B, int Lq, int Lk, int d_model, int h,
+                    int d_k, int d_v,
+                    const void* x_q, const void* x_kv,
+                    const void* w_q, const void* w_k, const void* w_v,
+                    void* q, void* k, void* v, hipStream_t stream);
+
+/*
+ * mha_out_proj -- MultiHead = Concat(head_1, ..., head_h) W^O ([Deep]
+ * section 04, MultiHead equation; [Slides] slide "Multi-Head Attention").
+ *
+ *   o    [B, Lq, h, d_v] = [B*Lq, h*d_v]   the attention output (BLHD)
+ *   w_o  [h*d_v, d_model]
+ *   y    [B, Lq, d_model]                  output; must not overlap o, w_o
+ *
+ * Supported: MHA_BF16 and MHA_F32; d_model % 64 == 0, h*d_v % 64 == 0.
+ */
+int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
+                 const void* o, const void* w_o, void* y, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* mha_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H */

@@ -1,0 +1,107 @@
+"""The C ABI of libmha.so, checked without a GPU.
+
+The library must load and export every function include/mha.h declares, and
+its argument validation -- which runs before any HIP call -- must reject bad
+calls with the documented status codes.  Nothing here launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_scaled_dot_fwd_amd as mha
+
+OK, INVALID, UNSUPPORTED, LAUNCH = 0, 1, 2, 3
+BF16, F32 = 1, 0
+FAKE = 0x1000  # a 16-byte aligned non-NULL address; never dereferenced here
+
+
+def declared_functions():
+    text = open(mha.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mha_\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mha.LIBRARY):
+        from transformer_scaled_dot_fwd_amd import build
+        build.build()
+    return mha.lib()
+
+
+def test_header_declares_the_boundary():
+    assert set(declared_functions()) == {"mha_forward", "mha_project_qkv", "mha_out_proj",
+                                         "mha_status_string"}
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in (OK, INVALID, UNSUPPORTED, LAUNCH, 99):
+        assert L.mha_status_string(s)
+    assert L.mha_status_string(OK) == b"ok"
+
+
+def fwd(L, dt=BF16, B=2, h=2, Lq=8, Lk=8, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, mask=0,
+        lens=None, o=FAKE):
+    return L.mha_forward(dt, B, h, Lq, Lk, dk, dv, q, k, v, mask, lens, o, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dt=7), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(h=0), INVALID),
+    (dict(Lq=-2), INVALID),
+    (dict(dk=0), INVALID),
+    (dict(mask=4), INVALID),
+    (dict(mask=2, Lq=8, Lk=9), INVALID),          # causal needs Lq == Lk
+    (dict(mask=1, lens=None), INVALID),           # key padding needs lengths
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(q=FAKE + 8), INVALID),                  # misaligned
+    (dict(dk=64, dv=32), UNSUPPORTED),
+    (dict(dk=32, dv=32), UNSUPPORTED),            # bf16 is built for d = 64
+    (dict(dt=F32, dk=24, dv=24), UNSUPPORTED),
+    (dict(B=0), OK),                              # empty: nothing launched
+    (dict(Lq=0, Lk=0, mask=2), OK),
+])
+def test_forward_validation(L, kw, expect):
+    assert fwd(L, **kw) == expect
+
+
+def test_project_and_out_proj_validation(L):
+    P = L.mha_project_qkv
+    # (dt, B, Lq, Lk, d_model, h, dk, dv, x_q, x_kv, wq, wk, wv, q, k, v, stream)
+    base = [BF16, 2, 8, 8, 512, 8, 64, 64] + [FAKE] * 8 + [None]
+    def call(**over):
+        a = list(base)
+        keys = ["dt", "B", "Lq", "Lk", "dm", "h", "dk", "dv", "xq", "xkv", "wq", "wk", "wv",
+                "q", "k", "v"]
+        for name, val in over.items():
+            a[keys.index(name)] = val
+        return P(*a)
+    assert call(dm=0) == INVALID
+    assert call(xq=None) == INVALID
+    assert call(wv=FAKE + 4) == INVALID
+    assert call(dk=64, dv=32) == UNSUPPORTED
+    assert call(dm=500) == UNSUPPORTED
+    assert call(h=3, dk=20, dv=20) == UNSUPPORTED
+    assert call(B=0) == OK
+    O = L.mha_out_proj
+    assert O(BF16, 2, 8, 8, 64, 512, None, FAKE, FAKE, None) == INVALID
+    assert O(BF16, 2, 8, 8, 64, 500, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert O(BF16, 0, 8, 8, 64, 512, FAKE, FAKE, FAKE, None) == OK
+    assert O(9, 2, 8, 8, 64, 512, FAKE, FAKE, FAKE, None) == INVALID
+
+
+def test_python_binding_checks_before_calling():
+    import torch
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):          # host tensors are refused
+        mha.mha_forward(q, q, q)

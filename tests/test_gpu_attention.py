@@ -1,0 +1,227 @@
+"""GPU parity of mha_forward (through the C ABI) against the fp64 oracle.
+
+Inputs come from the seeded generators; the oracle receives the same values
+upcast to fp64.  Small shapes are compared element by element over several
+tiles and ragged tails; the named workloads are compared in full where the
+oracle finishes in seconds, otherwise on sampled rows computed one by one,
+in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_scaled_dot_fwd_amd as mha
+from gpu_util import check, device, say, to_np
+from workloads import configs, generate
+
+pytestmark = pytest.mark.gpu
+
+NONE, PAD, CAUSAL = 0, 1, 2
+
+
+def make(B, h, Lq, Lk, d, dtype, seed):
+    q = generate.normal((B, Lq, h, d), seed, dtype)
+    k = generate.normal((B, Lk, h, d), seed + 1, dtype)
+    v = generate.normal((B, Lk, h, d), seed + 2, dtype)
+    return q, k, v
+
+
+def run(q, k, v, mask, lens, dev):
+    lens_d = lens.to(dev) if lens is not None else None
+    o = mha.mha_forward(q.to(dev), k.to(dev), v.to(dev), mask=mask, kv_lens=lens_d)
+    torch.cuda.synchronize()
+    return o
+
+
+def test_tiny_fp32_config():
+    dev = device()
+    w = configs.get("c1")
+    inp = configs.make_inputs(w)
+    say(f"case {w.name}")
+    o = run(inp["q"], inp["k"], inp["v"], w.mask, None, dev)
+    check(o, oracle.attention(inp["q"], inp["k"], inp["v"], mask=w.mask), "f32", w.name)
+
+
+@pytest.mark.parametrize("d", [8, 16, 32, 64])
+@pytest.mark.parametrize("mask", [NONE, PAD, CAUSAL, PAD | CAUSAL])
+def test_fp32_ragged(d, mask):
+    dev = device()
+    B, h = 2, 3
+    Lq = Lk = 130
+    if not mask & CAUSAL:
+        Lk = 77
+    say(f"case fp32 d={d} mask={mask} Lq={Lq} Lk={Lk}")
+    q, k, v = make(B, h, Lq, Lk, d, "f32", 500 + d + 10 * mask)
+    lens = torch.tensor([Lk - 3, 1], dtype=torch.int32)
+    o = run(q, k, v, mask, lens, dev)
+    check(o, oracle.attention(q, k, v, mask=mask, kv_lens=lens), "f32", f"fp32 d={d} m={mask}")
+
+
+@pytest.mark.parametrize("mask", [NONE, PAD, CAUSAL, PAD | CAUSAL])
+@pytest.mark.parametrize("shape", [(3, 2, 200, 177), (2, 3, 64, 64), (1, 1, 1, 1),
+                                   (2, 2, 5, 300), (1, 2, 257, 257)])
+def test_bf16_ragged(shape, mask):
+    dev = device()
+    B, h, Lq, Lk = shape
+    if mask & CAUSAL:
+        Lk = Lq
+    say(f"case bf16 B={B} h={h} Lq={Lq} Lk={Lk} mask={mask}")
+    q, k, v = make(B, h, Lq, Lk, 64, "bf16", 700 + Lq + 3 * Lk + mask)
+    choices = [Lk, 1, max(Lk - 1, 0), 0, Lk + 50, -5, Lk // 2, 65]
+    lens = torch.tensor([choices[i % len(choices)] for i in range(B)], dtype=torch.int32)
+    o = run(q, k, v, mask, lens, dev)
+    check(o, oracle.attention(q, k, v, mask=mask, kv_lens=lens), "bf16",
+          f"bf16 {shape} m={mask}")
+
+
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_named_workload_full(name):
+    dev = device()
+    w = configs.get(name)
+    say(f"case {w.name} (full compare)")
+    inp = configs.make_inputs(w)
+    o = run(inp["q"], inp["k"], inp["v"], w.mask, inp["kv_lens"], dev)
+    ref = oracle.attention(inp["q"], inp["k"], inp["v"], mask=w.mask, kv_lens=inp["kv_lens"])
+    check(o, ref, w.dtype, w.name)
+
+
+def sample_rows(B, h, L, n_random, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, L // 2, L - 2, L - 1]
+    rows = []
+    for b in range(B):
+        for t in range(h):
+            idx = [i for i in fixed if 0 <= i < L] + list(rng.integers(0, L, n_random))
+            rows += [(b, t, int(i)) for i in idx]
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["c5", "sweep_h8_L1024_nomask", "sweep_h16_L2048_causal",
+                                  "sweep_h8_L4096_nomask"])
+def test_named_workload_sampled(name):
+    dev = device()
+    w = configs.get(name)
+    say(f"case {w.name} (sampled rows)")
+    inp = configs.make_inputs(w)
+    o = run(inp["q"], inp["k"], inp["v"], w.mask, inp["kv_lens"], dev)
+    rows = sample_rows(w.B, w.h, w.Lq, 4, 99)
+    ref = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, mask=w.mask,
+                                kv_lens=inp["kv_lens"])
+    o_np = to_np(o)
+    got = np.stack([o_np[b, i, t] for (b, t, i) in rows])
+    check(got, ref, w.dtype, f"{w.name} ({len(rows)} rows)")
+
+
+# ---------------------------------------------------------------------------
+# Properties that hold at any size (bit-exact where the method fixes bits).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_padding_garbage_is_never_read(dtype):
+    """Rows of K/V at or beyond the length may hold anything (NaN, Inf,
+    1e30): O is bit-identical to the run with zeros there."""
+    dev = device()
+    B, h, L, d = 4, 2, 150, 64
+    q, k, v = make(B, h, L, L, d, dtype, 901)
+    lens = torch.tensor([150, 3, 64, 100], dtype=torch.int32)
+    k0, v0 = k.clone(), v.clone()
+    for b in range(B):
+        k0[b, lens[b]:] = 0
+        v0[b, lens[b]:] = 0
+    for mask in (PAD, PAD | CAUSAL):
+        base = run(q, k0, v0, mask, lens, dev)
+        for junk in (float("nan"), float("inf"), 1e30):
+            k2, v2 = k.clone(), v.clone()
+            for b in range(B):
+                k2[b, lens[b]:] = junk
+                v2[b, lens[b]:] = junk
+            o2 = run(q, k2, v2, mask, lens, dev)
+            assert torch.equal(o2, base), (dtype, mask, junk)
+
+
+def test_causal_prefix_is_unaffected_by_later_keys():
+    dev = device()
+    B, h, L, d = 2, 2, 300, 64
+    q, k, v = make(B, h, L, L, d, "bf16", 902)
+    base = run(q, k, v, CAUSAL, None, dev)
+    for t in (0, 63, 64, 200):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, t + 1:] = generate.normal(k2[:, t + 1:].shape, 903 + t, "bf16") * 50
+        v2[:, t + 1:] = generate.normal(v2[:, t + 1:].shape, 904 + t, "bf16") * 50
+        o2 = run(q, k2, v2, CAUSAL, None, dev)
+        assert torch.equal(o2[:, :t + 1], base[:, :t + 1]), t
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_key_and_empty_rows(dtype):
+    """One legal key: O is that V row bit-exactly; no legal key: O = 0."""
+    dev = device()
+    B, h, L, d = 3, 2, 70, 64
+    q, k, v = make(B, h, L, L, d, dtype, 905)
+    lens = torch.tensor([1, 0, 70], dtype=torch.int32)
+    o = run(q, k, v, PAD, lens, dev).cpu()
+    assert torch.equal(o[0], v[0, 0:1].expand(L, h, d))
+    assert torch.equal(o[1], torch.zeros(L, h, d, dtype=o.dtype))
+    oc = run(q, k, v, CAUSAL, None, dev).cpu()
+    assert torch.equal(oc[:, 0], v[:, 0])
+
+
+def test_empty_and_keyless_calls():
+    dev = device()
+    q, k, v = make(0, 2, 8, 8, 64, "bf16", 906)
+    o = mha.mha_forward(q.to(dev), k.to(dev), v.to(dev))
+    assert o.shape == (0, 8, 2, 64)
+    q, _, _ = make(2, 2, 8, 1, 64, "bf16", 907)
+    k = torch.zeros(2, 0, 2, 64, dtype=torch.bfloat16)
+    o = run(q, k, k.clone(), NONE, None, dev)
+    assert torch.equal(o.cpu(), torch.zeros(2, 8, 2, 64, dtype=torch.bfloat16))
+
+
+def test_uniform_and_constant_values():
+    """K = 0: every logit equal, O_i = mean of the legal V rows.
+    V = 1: O = 1 (weights sum to one)."""
+    dev = device()
+    B, h, L, d = 2, 2, 190, 64
+    q, k, v = make(B, h, L, L, d, "bf16", 908)
+    lens = torch.tensor([190, 77], dtype=torch.int32)
+    kz = torch.zeros_like(k)
+    for mask in (PAD, CAUSAL | PAD):
+        o = run(q, kz, v, mask, lens, dev)
+        check(o, oracle.attention(q, kz, v, mask=mask, kv_lens=lens), "bf16", f"K=0 m={mask}")
+        ones = torch.ones_like(v)
+        o1 = run(q, k, ones, mask, lens, dev)
+        assert torch.equal(o1.cpu(), torch.ones_like(o1.cpu()))
+
+
+def test_shift_invariance_large_logits():
+    """Adding u to every key shifts each logit row by q.u/8: the output is
+    unchanged within tolerance and stays finite for shifts of ~1e3."""
+    dev = device()
+    B, h, L, d = 2, 2, 256, 64
+    q, k, v = make(B, h, L, L, d, "bf16", 909)
+    u = torch.full((1, 1, h, d), 16.0, dtype=torch.bfloat16)   # exact in bf16
+    for mask in (NONE, CAUSAL):
+        o = run(q, k + u, v, mask, None, dev)
+        ref = oracle.attention(q, k + u, v, mask=mask)
+        check(o, ref, "bf16", f"shifted keys m={mask}")
+
+
+def test_repeat_runs_are_bit_identical():
+    dev = device()
+    w = configs.get("c2")
+    inp = configs.make_inputs(w, dev)
+    a = mha.mha_forward(inp["q"], inp["k"], inp["v"], mask=w.mask, kv_lens=inp["kv_lens"])
+    b = mha.mha_forward(inp["q"], inp["k"], inp["v"], mask=w.mask, kv_lens=inp["kv_lens"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_rejected_arguments_raise():
+    dev = device()
+    q, k, v = make(1, 1, 8, 9, 64, "bf16", 910)
+    with pytest.raises(mha.MHAError):
+        mha.mha_forward(q.to(dev), k.to(dev), v.to(dev), mask=CAUSAL)
+    q, k, v = make(1, 1, 8, 8, 48, "bf16", 911)
+    with pytest.raises(mha.MHAError):
+        mha.mha_forward(q.to(dev), k.to(dev), v.to(dev))

@@ -1,0 +1,194 @@
+"""Multi-head scaled dot-product attention forward for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libmha.so``, whose C ABI is ``include/mha.h``.
+The functions carry the C names; they only check and marshal arguments
+(torch tensors -> device pointers, torch's current HIP stream -> hipStream_t)
+and raise on a non-zero status.  Every step of the computation runs in the
+library's HIP kernels; there is no CPU or PyTorch fallback, and a missing
+library raises at the first call.
+
+    mha_forward(q, k, v, mask, kv_lens)          O = softmax(QK^T/sqrt(d_k) + M) V
+    mha_project_qkv(x_q, x_kv, w_q, w_k, w_v, h)  Q, K, V = X_q W^Q, X_kv W^K, X_kv W^V
+    mha_out_proj(o, w_o)                          Y = Concat(heads) W^O
+    mha_block(...)                                the three above in sequence
+
+Tensors are CUDA (HIP) tensors, contiguous, all of one dtype (torch.bfloat16
+or torch.float32); q/k/v/o use the BLHD layout [B, L, h, d].  ``kv_lens`` is
+an int32 device tensor [B].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+MASK_NONE = 0
+MASK_KEY_PADDING = 1
+MASK_CAUSAL = 2
+
+MHA_F32 = 0
+MHA_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libmha.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "mha.h")
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmha.so (ctypes), with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(
+            f"{LIBRARY} is not built; run `python -m transformer_scaled_dot_fwd_amd.build` "
+            "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIBRARY)
+    i, p = ctypes.c_int, ctypes.c_void_p
+    L.mha_forward.argtypes = [i, i, i, i, i, i, i, p, p, p, i, p, p, p]
+    L.mha_forward.restype = i
+    L.mha_project_qkv.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
+    L.mha_project_qkv.restype = i
+    L.mha_out_proj.argtypes = [i, i, i, i, i, i, p, p, p, p]
+    L.mha_out_proj.restype = i
+    L.mha_status_string.argtypes = [i]
+    L.mha_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+class MHAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().mha_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MHA_BF16
+    if t.dtype == torch.float32:
+        return MHA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _check(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def mha_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: int = MASK_NONE,
+                kv_lens: torch.Tensor | None = None, out: torch.Tensor | None = None
+                ) -> torch.Tensor:
+    """O = softmax(Q K^T / sqrt(d_k) + M) V; q [B,Lq,h,d_k], k [B,Lk,h,d_k],
+    v [B,Lk,h,d_v] -> o [B,Lq,h,d_v]."""
+    _check(q, "q")
+    _check(k, "k", q.dtype)
+    _check(v, "v", q.dtype)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, L, h, d]")
+    B, Lq, h, dk = q.shape
+    Lk = k.shape[1]
+    dv = v.shape[3]
+    if k.shape != (B, Lk, h, dk) or v.shape[:3] != (B, Lk, h):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}")
+    lens_ptr = None
+    if mask & MASK_KEY_PADDING:
+        if kv_lens is None:
+            raise ValueError("key padding needs kv_lens")
+        _check(kv_lens, "kv_lens", torch.int32)
+        if kv_lens.shape != (B,):
+            raise ValueError(f"kv_lens must have shape ({B},)")
+        lens_ptr = kv_lens.data_ptr()
+    if out is None:
+        out = torch.empty((B, Lq, h, dv), dtype=q.dtype, device=q.device)
+    else:
+        _check(out, "out", q.dtype)
+        if out.shape != (B, Lq, h, dv):
+            raise ValueError("out has the wrong shape")
+    rc = lib().mha_forward(_dtype_code(q), B, h, Lq, Lk, dk, dv, q.data_ptr(), k.data_ptr(),
+                           v.data_ptr(), int(mask), lens_ptr, out.data_ptr(),
+                           _stream(q.device))
+    if rc != 0:
+        raise MHAError(rc, "mha_forward")
+    return out
+
+
+def mha_project_qkv(x_q: torch.Tensor, x_kv: torch.Tensor, w_q: torch.Tensor,
+                    w_k: torch.Tensor, w_v: torch.Tensor, h: int, out=None):
+    """Q = X_q W^Q, K = X_kv W^K, V = X_kv W^V as BLHD tensors.
+
+    x_q [B,Lq,d_model], x_kv [B,Lk,d_model] (pass x_q again for
+    self-attention), w_q/w_k [d_model, h*d_k], w_v [d_model, h*d_v]."""
+    for t, n in ((x_q, "x_q"), (x_kv, "x_kv"), (w_q, "w_q"), (w_k, "w_k"), (w_v, "w_v")):
+        _check(t, n, x_q.dtype)
+    B, Lq, dm = x_q.shape
+    Lk = x_kv.shape[1]
+    if x_kv.shape != (B, Lk, dm):
+        raise ValueError("x_kv shape mismatch")
+    nq, nv = w_q.shape[1], w_v.shape[1]
+    if w_q.shape != (dm, nq) or w_k.shape != (dm, nq) or w_v.shape[0] != dm:
+        raise ValueError("weight shape mismatch")
+    if nq % h or nv % h:
+        raise ValueError("projection width not divisible by h")
+    dk, dv = nq // h, nv // h
+    if out is None:
+        q = torch.empty((B, Lq, h, dk), dtype=x_q.dtype, device=x_q.device)
+        k = torch.empty((B, Lk, h, dk), dtype=x_q.dtype, device=x_q.device)
+        v = torch.empty((B, Lk, h, dv), dtype=x_q.dtype, device=x_q.device)
+    else:
+        q, k, v = out
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _check(t, n, x_q.dtype)
+    rc = lib().mha_project_qkv(_dtype_code(x_q), B, Lq, Lk, dm, h, dk, dv, x_q.data_ptr(),
+                               x_kv.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
+                               q.data_ptr(), k.data_ptr(), v.data_ptr(), _stream(x_q.device))
+    if rc != 0:
+        raise MHAError(rc, "mha_project_qkv")
+    return q, k, v
+
+
+def mha_out_proj(o: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor | None = None
+                 ) -> torch.Tensor:
+    """Y = Concat(head_1..head_h) W^O; o [B,Lq,h,d_v], w_o [h*d_v, d_model]."""
+    _check(o, "o")
+    _check(w_o, "w_o", o.dtype)
+    B, Lq, h, dv = o.shape
+    dm = w_o.shape[1]
+    if w_o.shape != (h * dv, dm):
+        raise ValueError("w_o shape mismatch")
+    if out is None:
+        out = torch.empty((B, Lq, dm), dtype=o.dtype, device=o.device)
+    else:
+        _check(out, "out", o.dtype)
+    rc = lib().mha_out_proj(_dtype_code(o), B, Lq, h, dv, dm, o.data_ptr(), w_o.data_ptr(),
+                            out.data_ptr(), _stream(o.device))
+    if rc != 0:
+        raise MHAError(rc, "mha_out_proj")
+    return out
+
+
+def mha_block(x_q, x_kv, w_q, w_k, w_v, w_o, h: int, mask: int = MASK_NONE, kv_lens=None):
+    """MultiHead(X_q, X_kv, X_kv) = Concat(head_1..head_h) W^O: three launches
+    on the current stream, no host synchronisation."""
+    q, k, v = mha_project_qkv(x_q, x_kv, w_q, w_k, w_v, h)
+    o = mha_forward(q, k, v, mask=mask, kv_lens=kv_lens)
+    return mha_out_proj(o, w_o)

@@ -1,0 +1,69 @@
+// device.h -- gfx950 (CDNA4) primitives shared by the attention and GEMM
+// kernels: vector types, the bf16 MFMA, the LDS transpose read, and
+// cross-half-wave exchange.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// D = A B + C on a 32x32x16 bf16 tile, fp32 accumulate.
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. 8*(l/32)+7
+//   B (16 x 32): lane l holds column l%32, k = 8*(l/32) .. 8*(l/32)+7
+//   D (32 x 32): lane l holds column l%32, rows
+//                (r%4) + 8*(r/4) + 4*(l/32) for register r = 0..15
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator that register r of this lane holds.
+__device__ __forceinline__ constexpr int acc_row(int r, int half) {
+    return (r & 3) + 8 * (r >> 2) + 4 * half;
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Inside each group of 16 lanes,
+// lane 4*r + c points at 4 consecutive bf16 of "row" r (columns 4c..4c+3 of
+// a 4 x 16 block); lane j of the group receives column j of that block:
+// the 4 elements (row 0..3, column j).
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// v_permlane32_swap(x, x) exchanges the upper half of the first operand with
+// the lower half of the second: lane l < 32 gets (x[l], x[l+32]) and lane
+// l >= 32 gets (x[l-32], x[l]).  A symmetric reduction of the pair therefore
+// combines lanes l and l ^ 32 with identical bits in both.
+__device__ __forceinline__ float max_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+    bf16x8 z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+    return z;
+}
+
+__device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+}  // namespace mha

@@ -1,0 +1,37 @@
+// launch.h -- host-side launchers of the device kernels (internal to
+// libmha.so; the public C ABI is include/mha.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+struct AttnArgs {
+    int B, H, Lq, Lk, D;
+    int mask;                 // bit 0: key padding, bit 1: causal
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* kv_lens;   // device, [B]; only read with key padding
+    void* o;
+};
+
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
+
+// One GEMM problem Y[M, N] = X[M, K] W[K, N] (row-major).
+struct GemmProblem {
+    const void* x;
+    const void* w;
+    void* y;
+    int M;
+};
+
+// Up to three independent problems sharing N and K, in one launch.
+hipError_t launch_gemm_bf16(const GemmProblem* probs, int n_probs, int N, int K,
+                            hipStream_t stream);
+hipError_t launch_gemm_f32(const GemmProblem* probs, int n_probs, int N, int K,
+                           hipStream_t stream);
+
+}  // namespace mha

@@ -1,0 +1,107 @@
+// mha_api.hip -- the extern "C" boundary of libmha.so (declared in
+// include/mha.h): argument validation, dispatch to the compiled kernels and
+// launch on the caller's stream.  Validation finishes before the first HIP
+// call, so a rejected call touches neither the device nor any buffer.
+#include <limits.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "mha.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MHA_OK : MHA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mha_status_string(int status) {
+    switch (status) {
+        case MHA_OK: return "ok";
+        case MHA_ERR_INVALID_ARG: return "invalid argument";
+        case MHA_ERR_UNSUPPORTED: return "unsupported dtype or shape (not compiled)";
+        case MHA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v, const void* q,
+                const void* k, const void* v, int mask_flags, const int32_t* kv_lens, void* o,
+                hipStream_t stream) {
+    if (dt != MHA_F32 && dt != MHA_BF16) return MHA_ERR_INVALID_ARG;
+    if (B < 0 || h < 1 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1) return MHA_ERR_INVALID_ARG;
+    if (mask_flags & ~(MHA_MASK_KEY_PADDING | MHA_MASK_CAUSAL)) return MHA_ERR_INVALID_ARG;
+    if ((mask_flags & MHA_MASK_CAUSAL) && Lq != Lk) return MHA_ERR_INVALID_ARG;
+    if (B == 0 || Lq == 0) return MHA_OK;  // empty output: nothing to do
+    if (!q || !o) return MHA_ERR_INVALID_ARG;
+    if (Lk > 0 && (!k || !v)) return MHA_ERR_INVALID_ARG;
+    if ((mask_flags & MHA_MASK_KEY_PADDING) && !kv_lens) return MHA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(o) || (Lk > 0 && (!aligned16(k) || !aligned16(v))))
+        return MHA_ERR_INVALID_ARG;
+    if (d_k != d_v) return MHA_ERR_UNSUPPORTED;
+    if ((long long)B * h > INT_MAX) return MHA_ERR_UNSUPPORTED;
+    const long long tiles = (long long)B * h * ((Lq + 63) / 64);
+    if (tiles > INT_MAX) return MHA_ERR_UNSUPPORTED;
+
+    mha::AttnArgs a{B, h, Lq, Lk, d_k, mask_flags, q, k, v, kv_lens, o};
+    if (dt == MHA_BF16) {
+        if (d_k != 64) return MHA_ERR_UNSUPPORTED;
+        return launch_status(mha::launch_attention_bf16(a, stream));
+    }
+    if (d_k != 8 && d_k != 16 && d_k != 32 && d_k != 64) return MHA_ERR_UNSUPPORTED;
+    return launch_status(mha::launch_attention_f32(a, stream));
+}
+
+int mha_project_qkv(mha_dtype dt, int B, int Lq, int Lk, int d_model, int h, int d_k, int d_v,
+                    const void* x_q, const void* x_kv, const void* w_q, const void* w_k,
+                    const void* w_v, void* q, void* k, void* v, hipStream_t stream) {
+    if (dt != MHA_F32 && dt != MHA_BF16) return MHA_ERR_INVALID_ARG;
+    if (B < 0 || Lq < 0 || Lk < 0 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1)
+        return MHA_ERR_INVALID_ARG;
+    const long long Mq = (long long)B * Lq, Mkv = (long long)B * Lk;
+    if (Mq == 0 && Mkv == 0) return MHA_OK;
+    if (Mq > 0 && (!x_q || !w_q || !q)) return MHA_ERR_INVALID_ARG;
+    if (Mkv > 0 && (!x_kv || !w_k || !w_v || !k || !v)) return MHA_ERR_INVALID_ARG;
+    const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, q, k, v};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MHA_ERR_INVALID_ARG;
+    if (d_k != d_v) return MHA_ERR_UNSUPPORTED;
+    const long long N = (long long)h * d_k;
+    if (d_model % 64 != 0 || N % 64 != 0 || N > INT_MAX) return MHA_ERR_UNSUPPORTED;
+    if (Mq > INT_MAX || Mkv > INT_MAX) return MHA_ERR_UNSUPPORTED;
+
+    mha::GemmProblem probs[3];
+    int n = 0;
+    if (Mq > 0) probs[n++] = {x_q, w_q, q, (int)Mq};
+    if (Mkv > 0) {
+        probs[n++] = {x_kv, w_k, k, (int)Mkv};
+        probs[n++] = {x_kv, w_v, v, (int)Mkv};
+    }
+    const hipError_t e = (dt == MHA_BF16)
+                             ? mha::launch_gemm_bf16(probs, n, (int)N, d_model, stream)
+                             : mha::launch_gemm_f32(probs, n, (int)N, d_model, stream);
+    return launch_status(e);
+}
+
+int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model, const void* o,
+                 const void* w_o, void* y, hipStream_t stream) {
+    if (dt != MHA_F32 && dt != MHA_BF16) return MHA_ERR_INVALID_ARG;
+    if (B < 0 || Lq < 0 || h < 1 || d_v < 1 || d_model < 1) return MHA_ERR_INVALID_ARG;
+    const long long M = (long long)B * Lq;
+    if (M == 0) return MHA_OK;
+    if (!o || !w_o || !y) return MHA_ERR_INVALID_ARG;
+    if (!aligned16(o) || !aligned16(w_o) || !aligned16(y)) return MHA_ERR_INVALID_ARG;
+    const long long K = (long long)h * d_v;
+    if (d_model % 64 != 0 || K % 64 != 0 || K > INT_MAX || M > INT_MAX)
+        return MHA_ERR_UNSUPPORTED;
+    mha::GemmProblem prob{o, w_o, y, (int)M};
+    const hipError_t e = (dt == MHA_BF16)
+                             ? mha::launch_gemm_bf16(&prob, 1, d_model, (int)K, stream)
+                             : mha::launch_gemm_f32(&prob, 1, d_model, (int)K, stream);
+    return launch_status(e);
+}
+
+}  // extern "C"
