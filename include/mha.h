@@ -87,7 +87,9 @@ enum {
  * with no legal key (kv_lens[b] == 0) outputs exactly 0.  Padded query rows
  * are computed like any other row.
  *
- * Supported: B, h, Lq, Lk >= 1 (B*h*ceil(Lq/128) < 2^31), d_k == d_v;
+ * Supported: B, Lq, Lk >= 0 and h >= 1 (B == 0 or Lq == 0 is a no-op;
+ * Lk == 0 gives O = 0), d_k == d_v, B*h*ceil(Lq/64) < 2^31, and one batch
+ * row of Q or of K/V under 2 GiB (L*h*d_k*elem_size < 2^31);
  * MHA_BF16 with d_k = 64; MHA_F32 with d_k in {8, 16, 32, 64}.
  */
 int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v,

@@ -20,41 +20,52 @@ namespace mha {
 // ---------------------------------------------------------------------------
 // bf16, d = 64: MFMA path.
 //
-// Workgroup = 4 waves = one (batch row, head, tile of 128 queries); wave w
-// owns queries q0 + 32w .. q0 + 32w + 31, one query per lane column.  Key/
-// value tiles of 64 rows are staged through LDS and shared by the 4 waves.
+// Workgroup = NW waves = one (batch row, head, tile of 64*NW queries).  Wave
+// w owns queries q0 + 64w .. q0 + 64w + 63 as two blocks of 32, one query
+// per lane column.  Key/value tiles of 32 rows pass through a 3-stage LDS
+// ring shared by the waves (one barrier per tile):
 //
-//   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, A = K rows (LDS, 16-byte
+//   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, A = K rows (16-byte LDS
 //                      reads), B = Q (registers, loaded once)
 //   O^T += V^T P^T     A = V^T (LDS transpose reads), B = P (registers)
 //
-// Keeping the query in the lane column makes every per-query quantity (row
-// max, row sum, rescale factor) lane-local, with one exchange between the
-// two half-waves.  The PV contraction runs over keys in the order the S^T
-// accumulator holds them, and the V^T transpose reads fetch V rows in that
-// same order.
+// Each A operand (a K or V^T fragment) feeds both query blocks, so LDS
+// traffic is 4 bytes per (query, key) pair.  Keeping the query in the lane
+// column makes every per-query quantity (row max, row sum, rescale factor)
+// lane-local, with one exchange between the two half-waves.  The PV
+// contraction runs over keys in the order the S^T accumulator holds them,
+// and the V^T transpose reads fetch V rows in that same order.
+//
+// Software pipeline per wave: while the softmax of tile j runs on the VALU,
+// the MFMAs of S for tile j+1 are already issued; then P_j V_j.  Global
+// loads run two tiles ahead through registers.
 // ---------------------------------------------------------------------------
 namespace {
 
 constexpr int D64 = 64;
-constexpr int BM = 128;          // queries per workgroup
-constexpr int BN = 64;           // keys per tile
-constexpr int KV_STRIDE = D64 + 8;  // LDS row pitch in elements (144 B)
-constexpr int THREADS = 256;
+constexpr int KT = 32;             // keys per tile
+constexpr int STAGES = 3;          // LDS ring depth
+constexpr int PITCH = D64 + 8;     // LDS row pitch in elements (144 B)
+constexpr int TILE = KT * PITCH;   // elements per K (or V) tile in LDS
 
-template <bool PAD, bool CAUSAL>
-__global__ __launch_bounds__(THREADS, 2) void attn_fwd_bf16_d64(
+template <int NW, bool PAD, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
     int n_qtiles, float scale_log2e) {
-    __shared__ __attribute__((aligned(16))) bf16 sK[BN * KV_STRIDE];
-    __shared__ __attribute__((aligned(16))) bf16 sV[BN * KV_STRIDE];
+    constexpr int BM = 64 * NW;
+    constexpr int THREADS = 64 * NW;
+    constexpr int CHUNKS = KT * D64 / 8 / THREADS;  // 16-byte chunks of K (and of V) per thread
+    __shared__ __attribute__((aligned(16))) bf16 sK[STAGES * TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sV[STAGES * TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5;
     const int l32 = lane & 31;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
 
     // Tile decode.  Causal: the longest query tiles are launched first.
     const int nbh = B * H;
@@ -74,7 +85,13 @@ __global__ __launch_bounds__(THREADS, 2) void attn_fwd_bf16_d64(
     if (PAD) kv_end = min(max(kv_lens[b], 0), Lk);
     int key_end = kv_end;
     if (CAUSAL) key_end = min(key_end, min(q0 + BM, Lq));
-    const int n_tiles = (key_end + BN - 1) / BN;
+    const int n_tiles = (key_end + KT - 1) / KT;
+
+    // Tiles this wave computes: none if it holds no query row; causal stops
+    // at the tile holding the wave's last query.
+    const int wq0 = q0 + 64 * wave;
+    int n_mine = (wq0 < Lq) ? n_tiles : 0;
+    if (CAUSAL) n_mine = min(n_mine, (wq0 + 64 + KT - 1) / KT);
 
     const size_t rs = (size_t)H * D64;  // elements between consecutive positions
     const bf16* qp = q + ((size_t)b * Lq * H + hh) * D64;
@@ -82,167 +99,245 @@ __global__ __launch_bounds__(THREADS, 2) void attn_fwd_bf16_d64(
     const bf16* vp = v + ((size_t)b * Lk * H + hh) * D64;
     bf16* op = o + ((size_t)b * Lq * H + hh) * D64;
 
-    // Q as the B operand of S^T = K Q^T: lane holds query l32, d = 16kk + 8half .. +7.
-    const int wq0 = q0 + 32 * wave;
-    const int my_q = wq0 + l32;
-    bf16x8 qop[4];
+    // Q as the B operand of S^T = K Q^T: block qb, lane holds query
+    // wq0 + 32qb + l32, d = 16kk + 8half .. +7.  Rows past Lq read as zeros.
+    const __amdgpu_buffer_rsrc_t qrsrc =
+        make_rsrc(qp, (uint32_t)(((size_t)(Lq - 1) * rs + D64) * sizeof(bf16)));
+    bf16x8 qop[2][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        qop[kk] = (my_q < Lq) ? *(const bf16x8*)(qp + (size_t)my_q * rs + 16 * kk + 8 * half)
-                              : zero_bf16x8();
-
-    f32x16 acc[2];
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qi = wq0 + 32 * qb + l32;
+        const uint32_t qoff =
+            qi < Lq ? (uint32_t)(((size_t)qi * rs + 8 * half) * sizeof(bf16)) : OOB_OFFSET;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-    float m_run = -INFINITY;  // running max of the raw logits q.k
-    float l_part = 0.0f;      // this lane's share of the row sum
-
-    // Cooperative tile load: 64 rows x 128 B of K and of V, 16 B per chunk,
-    // 2 chunks of each per thread.  Rows at or past kv_end are zero-filled
-    // and never read from memory.
-    bf16x8 kreg[2], vreg[2];
-    auto gload = [&](int t) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = tid + THREADS * u;
-            const int row = c >> 3;
-            const int col = (c & 7) * 8;
-            const int key = t * BN + row;
-            if (key < kv_end) {
-                kreg[u] = *(const bf16x8*)(kp + (size_t)key * rs + col);
-                vreg[u] = *(const bf16x8*)(vp + (size_t)key * rs + col);
-            } else {
-                kreg[u] = zero_bf16x8();
-                vreg[u] = zero_bf16x8();
-            }
-        }
-    };
-    auto sstore = [&]() {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = tid + THREADS * u;
-            const int row = c >> 3;
-            const int col = (c & 7) * 8;
-            *(bf16x8*)(sK + row * KV_STRIDE + col) = kreg[u];
-            *(bf16x8*)(sV + row * KV_STRIDE + col) = vreg[u];
-        }
-    };
-
-    if (n_tiles > 0) gload(0);
-    for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();  // every wave is done reading the previous tile
-        sstore();
-        __syncthreads();
-        if (t + 1 < n_tiles) gload(t + 1);  // in flight while this tile computes
-
-        const int k0 = t * BN;
-        if (wq0 >= Lq) continue;                // this wave holds no query rows
-        if (CAUSAL && k0 > wq0 + 31) continue;  // the whole tile is in this wave's future
-
-        // ---- S^T = K Q^T for keys k0 .. k0+63 (two 32-key blocks) ----
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 a =
-                    *(const bf16x8*)(sK + (32 * kb + l32) * KV_STRIDE + 16 * kk + 8 * half);
-                s[kb] = mfma32(a, qop[kk], s[kb]);
-            }
-        }
-
-        // ---- mask (boundary tiles only): select -inf at illegal keys ----
-        const bool need_mask = (k0 + BN > kv_end) || (CAUSAL && k0 + BN - 1 > wq0);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + acc_row(r, half);
-                    bool legal = key < kv_end;
-                    if (CAUSAL) legal = legal && key <= my_q;
-                    s[kb][r] = legal ? s[kb][r] : -INFINITY;
-                }
-        }
-
-        // ---- online softmax ----
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = max_halves(mx);
-        const float m_new = fmaxf(m_run, mx);
-        if (m_new > m_run) {
-            // m_run = -inf gives alpha = exp2(-inf) = 0: nothing accumulated yet.
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e);
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-            l_part *= alpha;
-            m_run = m_new;
-        }
-        const float mc = (m_run == -INFINITY) ? 0.0f : m_run * scale_log2e;
-
-        // p = exp2(s * c - m * c) = exp(s/sqrt(d) - m/sqrt(d)), rounded to bf16;
-        // the row sum accumulates the rounded p, the values PV actually uses.
-        bf16x8 pop[4];  // P^T chunk kc = 2*kb + c: registers 8c .. 8c+7 of s[kb]
-        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + e], scale_log2e, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(s[kb][8 * c + e + 1], scale_log2e, -mc));
-                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                    pop[2 * kb + c][e] = pp[0];
-                    pop[2 * kb + c][e + 1] = pp[1];
-                    l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part, false);
-                }
-
-        // ---- O^T += V^T P^T ----
-        // P chunk kc covers keys k0 + 16kc + {0..3, 8..11} (k = 0..7, lanes < 32)
-        // and k0 + 16kc + {4..7, 12..15} (k = 8..15, lanes >= 32).  The matching
-        // V^T operand: lane group g = lane/16 reads columns 32db + 16(g&1) + j
-        // of rows base + 0..3 and base + 8 .. 11, base = 16kc + 4(g>>1).
-        const int g = lane >> 4;
-        const int i16 = lane & 15;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            const int base = 16 * kc + 4 * (g >> 1) + (i16 >> 2);
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                const int col = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
-                const bf16x4 lo = lds_read_tr(sV + base * KV_STRIDE + col);
-                const bf16x4 hi = lds_read_tr(sV + (base + 8) * KV_STRIDE + col);
-                acc[db] = mfma32(join(lo, hi), pop[kc], acc[db]);
-            }
-        }
+        for (int kk = 0; kk < 4; ++kk)
+            qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
     }
 
-    // ---- epilogue: O = acc / l, or 0 for a row with no legal key ----
-    const float l_tot = sum_halves(l_part);
-    const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-    if (my_q < Lq) {
-        bf16* orow = op + (size_t)my_q * rs;
+    f32x16 acc[2][2];  // [query block][d block]
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                bf16x4 out;
+            for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
+    float m_run[2] = {-INFINITY, -INFINITY};  // running max of the raw logits q.k
+    float l_part[2] = {0.0f, 0.0f};           // this lane's share of the row sum
+
+    // Cooperative tile load: KT rows x 128 B of K and of V, 16 B per chunk,
+    // through buffer resources that end at the last legal key row: rows at
+    // or past kv_end read as zeros and are never fetched from memory.
+    const uint32_t kv_bytes =
+        kv_end > 0 ? (uint32_t)(((size_t)(kv_end - 1) * rs + D64) * sizeof(bf16)) : 0u;
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kp, kv_bytes);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vp, kv_bytes);
+    uint32_t voff[CHUNKS];  // this thread's chunk offsets inside a tile (loop invariant)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[db][4 * rg + e] * inv);
-                *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * half) = out;
+    for (int u = 0; u < CHUNKS; ++u) {
+        const int c = tid + THREADS * u;
+        voff[u] = (uint32_t)(((size_t)(c >> 3) * rs + (c & 7) * 8) * sizeof(bf16));
+    }
+    const uint32_t tile_bytes = (uint32_t)((size_t)KT * rs * sizeof(bf16));
+    bf16x8 kreg[CHUNKS], vreg[CHUNKS];
+    // Unconditional (branch-free) tile load; tiles at or past n_tiles read
+    // zeros without touching memory.
+    auto gload = [&](int t) {
+        const uint32_t base = t < n_tiles ? (uint32_t)t * tile_bytes : OOB_OFFSET;
+#pragma unroll
+        for (int u = 0; u < CHUNKS; ++u) {
+            kreg[u] = buffer_load16(krsrc, base + voff[u]);
+            vreg[u] = buffer_load16(vrsrc, base + voff[u]);
+        }
+    };
+    auto sstore = [&](int stage) {
+#pragma unroll
+        for (int u = 0; u < CHUNKS; ++u) {
+            const int c = tid + THREADS * u;
+            const int off = stage * TILE + (c >> 3) * PITCH + (c & 7) * 8;
+            *(bf16x8*)(sK + off) = kreg[u];
+            *(bf16x8*)(sV + off) = vreg[u];
+        }
+    };
+
+    // S^T for one tile: S[qb] (32 keys x 32 queries) from the K tile in LDS.
+    auto scores = [&](int stage, f32x16 (&S)[2]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[qb][r] = 0.0f;
+        const bf16* kt = sK + stage * TILE + l32 * PITCH + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 a = *(const bf16x8*)(kt + 16 * kk);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) S[qb] = mfma32(a, qop[qb][kk], S[qb]);
+        }
+    };
+
+    // Online softmax, step 1: mask tile t (boundary tiles only), take the
+    // row maxima and, when a row's maximum grew by more than 2^8 in exp2
+    // units, rescale that row's partial output and sum.  Between rescales
+    // the exponent offset m_run is a stale maximum, so p = exp2((s - m) c)
+    // stays below 2^8: the ratio acc / l is unaffected (softmax(x) =
+    // softmax(x - c) for any c), and bf16/fp32 have range to spare.
+    auto mask_and_max = [&](int t, f32x16 (&S)[2]) {
+        const int k0 = t * KT;
+        const bool need_mask = (k0 + KT > kv_end) || (CAUSAL && k0 + KT - 1 > wq0);
+        if (need_mask) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int qi = wq0 + 32 * qb + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + acc_row(r, half);
+                    bool legal = key < kv_end;
+                    if (CAUSAL) legal = legal && key <= qi;
+                    S[qb][r] = legal ? S[qb][r] : -INFINITY;
+                }
             }
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float mx = S[qb][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[qb][r]);
+            mx = max_halves(mx);
+            // True when m_run = -inf and the tile holds a legal key; false
+            // (NaN compare) while every key so far is masked.
+            const bool grow = (mx - m_run[qb]) * scale_log2e > 8.0f;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float m_new = grow ? mx : m_run[qb];
+                // m_run = -inf gives alpha = exp2(-inf) = 0: nothing accumulated yet.
+                const float alpha =
+                    grow ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * scale_log2e) : 1.0f;
+#pragma unroll
+                for (int db = 0; db < 2; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+                l_part[qb] *= alpha;
+                m_run[qb] = m_new;
+            }
+        }
+    };
+
+    // Online softmax, step 2, for two values of S[qb]: p = exp2(s c - m c) =
+    // exp((s - m)/sqrt(d)), rounded to bf16 into the P operand; the row sum
+    // accumulates the rounded p, the values PV actually uses.
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    auto exp_pair = [&](const f32x16 (&S)[2], const float (&mc)[2], bf16x8 (&pop)[2][2], int qb,
+                        int i) {
+        const int e = 2 * i;  // register index in S[qb]; chunk e/8, slot e%8
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][e], scale_log2e, -mc[qb]));
+        const float p1 =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][e + 1], scale_log2e, -mc[qb]));
+        const bf16x2 pp = {(bf16)p0, (bf16)p1};
+        pop[qb][e >> 3][e & 7] = pp[0];
+        pop[qb][e >> 3][(e & 7) + 1] = pp[1];
+        l_part[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part[qb], false);
+    };
+
+    // One tile of the pipeline: S for tile j+1 and P_j V_j on the MFMA pipe,
+    // the exponentiation of tile j on the VALU, hand-interleaved one MFMA per
+    // two p values (sched_barrier fences keep the order).
+    const f32x16 zero16 = {};
+    auto tile_step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+        // LDS operands, issued up front: K of tile j+1, V^T of tile j.  P
+        // chunk c covers keys 16c + {0..3, 8..11} (k = 0..7, lanes < 32) and
+        // 16c + {4..7, 12..15} (k = 8..15, lanes >= 32); the matching V^T
+        // operand: lane group g reads columns 32db + 16(g&1) + j of rows
+        // base + 0..3 and base + 8..11, base = 16c + 4(g>>1).
+        const bf16* kt = sK + ((j + 1) % STAGES) * TILE + l32 * PITCH + 8 * half;
+        bf16x8 ka[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[kk] = *(const bf16x8*)(kt + 16 * kk);
+        const bf16* vt = sV + (j % STAGES) * TILE;
+        bf16x8 va[2][2];  // [chunk][d block]
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int row = 16 * c + 4 * (g >> 1) + (i16 >> 2);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+                const int col = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
+                va[c][db] = join(lds_read_tr(vt + row * PITCH + col),
+                                 lds_read_tr(vt + (row + 8) * PITCH + col));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        mask_and_max(j, Scur);
+        float mc[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+            mc[qb] = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb] * scale_log2e;
+        bf16x8 pop[2][2];  // P^T operands [query block][16-key chunk]
+
+        // S_{j+1} (8 MFMAs) against the exponentials of query block 0.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int qb = i & 1, kk = i >> 1;
+            Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
+            exp_pair(Scur, mc, pop, 0, i);
+        }
+        // P_j V_j for query block 0, then block 1 as its chunks complete.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < 4) {
+                acc[0][i & 1] = mfma32(va[i >> 1][i & 1], pop[0][i >> 1], acc[0][i & 1]);
+            } else if (i < 6) {
+                acc[1][i & 1] = mfma32(va[0][i & 1], pop[1][0], acc[1][i & 1]);
+            }
+            exp_pair(Scur, mc, pop, 1, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc[1][0] = mfma32(va[1][0], pop[1][1], acc[1][0]);
+        acc[1][1] = mfma32(va[1][1], pop[1][1], acc[1][1]);
+    };
+
+    // ---- prologue: tiles 0 and 1 into the ring, tile 2 into registers ----
+    gload(0);
+    sstore(0);
+    gload(1);
+    sstore(1);
+    gload(2);
+    __syncthreads();
+
+    f32x16 SA[2], SB[2];
+    if (0 < n_mine) scores(0, SA);
+
+    // ---- main loop, unrolled by two so the score buffers alternate ----
+    auto iteration = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+        __syncthreads();  // tile j+1 is stored; everyone is done with tile j-1
+        sstore((j + 2) % STAGES);
+        gload(j + 3);
+        // Past a wave's last tile, S_{j+1} reads a zero or unused stage and
+        // is dropped.
+        if (j < n_mine) tile_step(j, Scur, Snext);
+    };
+    for (int j = 0; j < n_tiles; j += 2) {
+        iteration(j, SA, SB);
+        if (j + 1 < n_tiles) iteration(j + 1, SB, SA);
+    }
+
+    // ---- epilogue: O = acc / l, or 0 for a row with no legal key ----
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const float l_tot = sum_halves(l_part[qb]);
+        const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+        const int qi = wq0 + 32 * qb + l32;
+        if (qi < Lq) {
+            bf16* orow = op + (size_t)qi * rs;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    bf16x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[qb][db][4 * rg + e] * inv);
+                    *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * half) = out;
+                }
+        }
     }
 }
 
@@ -359,13 +454,12 @@ hipError_t launch_f32_d(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-}  // namespace
-
-int attention_qtile_rows(int dtype) { return dtype == 1 ? BM : F32_BM; }
-
-hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
+template <int NW>
+hipError_t launch_bf16_nw(const AttnArgs& a, hipStream_t stream) {
+    constexpr int BM = 64 * NW;
     const int n_qtiles = (a.Lq + BM - 1) / BM;
     const dim3 grid((unsigned)((long)a.B * a.H * n_qtiles));
+    const dim3 block(64 * NW);
     const float sl2e = (float)(1.4426950408889634 / sqrt((double)a.D));
     const bf16* q = (const bf16*)a.q;
     const bf16* k = (const bf16*)a.k;
@@ -373,23 +467,30 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     bf16* o = (bf16*)a.o;
     switch (a.mask) {
         case 0:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<false, false>), grid, dim3(THREADS), 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, false, false>), grid, block, 0, stream, q, k,
+                               v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         case 1:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<true, false>), grid, dim3(THREADS), 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, true, false>), grid, block, 0, stream, q, k,
+                               v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         case 2:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<false, true>), grid, dim3(THREADS), 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, false, true>), grid, block, 0, stream, q, k,
+                               v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         default:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<true, true>), grid, dim3(THREADS), 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, true, true>), grid, block, 0, stream, q, k,
+                               v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
+    // Four waves (256 queries) per workgroup share each K/V tile.
+    return launch_bf16_nw<4>(a, stream);
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {

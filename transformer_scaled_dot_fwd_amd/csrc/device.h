@@ -55,6 +55,24 @@ __device__ __forceinline__ float sum_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Buffer resource over [base, base + bytes): a buffer load whose bytes lie
+// past `bytes` returns zeros instead of touching memory.  (gfx9 descriptor
+// word 3: 32-bit data format, no swizzle.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Byte offset that is out of range of every resource made here: a load
+// from it returns zeros without a memory access.
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+
+// 16-byte load at per-lane byte offset `off` (the range check applies to
+// this offset).
+__device__ __forceinline__ bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;
 #pragma unroll

@@ -45,6 +45,11 @@ int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v, co
     if ((long long)B * h > INT_MAX) return MHA_ERR_UNSUPPORTED;
     const long long tiles = (long long)B * h * ((Lq + 63) / 64);
     if (tiles > INT_MAX) return MHA_ERR_UNSUPPORTED;
+    // Kernels address one batch row's Q, K or V slab with 32-bit byte
+    // offsets below 2^31.
+    const long long row_bytes = (long long)h * d_k * (dt == MHA_BF16 ? 2 : 4);
+    if ((long long)Lq * row_bytes >= (1LL << 31) || (long long)Lk * row_bytes >= (1LL << 31))
+        return MHA_ERR_UNSUPPORTED;
 
     mha::AttnArgs a{B, h, Lq, Lk, d_k, mask_flags, q, k, v, kv_lens, o};
     if (dt == MHA_BF16) {
