@@ -20,26 +20,36 @@ namespace mha {
 // ---------------------------------------------------------------------------
 // bf16, d = 64: MFMA path.
 //
-// Workgroup = NW waves = one (batch row, head, tile of 64*NW queries).  Wave
-// w owns queries q0 + 64w .. q0 + 64w + 63 as two blocks of 32, one query
-// per lane column.  Key/value tiles of 32 rows pass through a 3-stage LDS
-// ring shared by the waves (one barrier per tile):
+// Workgroup = NW waves = one (batch row, head, tile of 32*QB*NW queries).
+// Wave w owns QB blocks of 32 consecutive queries, one query per lane
+// column.  Key/value tiles of 32 rows pass through a 3-stage LDS ring shared
+// by the waves (one barrier per tile):
 //
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, A = K rows (16-byte LDS
 //                      reads), B = Q (registers, loaded once)
 //   O^T += V^T P^T     A = V^T (LDS transpose reads), B = P (registers)
 //
-// Each A operand (a K or V^T fragment) feeds both query blocks, so LDS
-// traffic is 4 bytes per (query, key) pair.  Keeping the query in the lane
-// column makes every per-query quantity (row max, row sum, rescale factor)
-// lane-local, with one exchange between the two half-waves.  The PV
-// contraction runs over keys in the order the S^T accumulator holds them,
-// and the V^T transpose reads fetch V rows in that same order.
+// Each A operand (a K or V^T fragment) feeds the wave's QB query blocks.
+// Keeping the query in the lane column makes every per-query quantity (row
+// max, row sum, rescale factor) lane-local, with one exchange between the
+// two half-waves.  The PV contraction runs over keys in the order the S^T
+// accumulator holds them, and the V^T transpose reads fetch V rows in that
+// same order.
 //
-// Software pipeline per wave: while the softmax of tile j runs on the VALU,
-// the MFMAs of S for tile j+1 are already issued; then P_j V_j.  Global
-// loads run two tiles ahead through registers.
+// Software pipeline per wave: the score MFMAs of tile j+1 and the PV MFMAs
+// of tile j are interleaved, one MFMA per two exponentials, with the
+// softmax VALU work of tile j.  Global loads run two tiles ahead.
 // ---------------------------------------------------------------------------
+#ifndef ATTN_QB
+#define ATTN_QB 2
+#endif
+#ifndef ATTN_QB1_OCC
+#define ATTN_QB1_OCC 3
+#endif
+#ifndef ATTN_NW
+#define ATTN_NW 4
+#endif
+
 namespace {
 
 constexpr int D64 = 64;
@@ -48,14 +58,16 @@ constexpr int STAGES = 3;          // LDS ring depth
 constexpr int PITCH = D64 + 8;     // LDS row pitch in elements (144 B)
 constexpr int TILE = KT * PITCH;   // elements per K (or V) tile in LDS
 
-template <int NW, bool PAD, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
+template <int NW, int QB, bool PAD, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_bf16_d64(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
     int n_qtiles, float scale_log2e) {
-    constexpr int BM = 64 * NW;
+    constexpr int WQ = 32 * QB;     // queries per wave
+    constexpr int BM = WQ * NW;     // queries per workgroup
     constexpr int THREADS = 64 * NW;
     constexpr int CHUNKS = KT * D64 / 8 / THREADS;  // 16-byte chunks of K (and of V) per thread
+    static_assert(CHUNKS >= 1 && KT * D64 / 8 == CHUNKS * THREADS, "tile load split");
     __shared__ __attribute__((aligned(16))) bf16 sK[STAGES * TILE];
     __shared__ __attribute__((aligned(16))) bf16 sV[STAGES * TILE];
 
@@ -67,15 +79,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
     const int g = lane >> 4;
     const int i16 = lane & 15;
 
-    // Tile decode.  Causal: the longest query tiles are launched first.
+    // Tile decode.  Workgroups are dispatched to the 8 XCDs round-robin
+    // (workgroup w runs on XCD w % 8); when B*H divides by 8, XCD x gets the
+    // (batch row, head) pairs x*nbh/8 .. (x+1)*nbh/8 - 1 whole, so every query
+    // tile of a pair shares that XCD's L2 for its K/V.  Causal: within each
+    // XCD the longest query tiles are launched first.
     const int nbh = B * H;
+    const int w = (int)blockIdx.x;
     int bh, qt;
-    if (CAUSAL) {
-        qt = n_qtiles - 1 - (int)(blockIdx.x / nbh);
-        bh = (int)(blockIdx.x % nbh);
+    if ((nbh & 7) == 0) {
+        const int x = w & 7, slot = w >> 3, per = nbh >> 3;
+        if (CAUSAL) {
+            qt = n_qtiles - 1 - slot / per;
+            bh = x * per + slot % per;
+        } else {
+            bh = x * per + slot / n_qtiles;
+            qt = slot % n_qtiles;
+        }
+    } else if (CAUSAL) {
+        qt = n_qtiles - 1 - w / nbh;
+        bh = w % nbh;
     } else {
-        bh = (int)(blockIdx.x / n_qtiles);
-        qt = (int)(blockIdx.x % n_qtiles);
+        bh = w / n_qtiles;
+        qt = w % n_qtiles;
     }
     const int b = bh / H;
     const int hh = bh - b * H;
@@ -89,9 +115,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
 
     // Tiles this wave computes: none if it holds no query row; causal stops
     // at the tile holding the wave's last query.
-    const int wq0 = q0 + 64 * wave;
+    const int wq0 = q0 + WQ * wave;
     int n_mine = (wq0 < Lq) ? n_tiles : 0;
-    if (CAUSAL) n_mine = min(n_mine, (wq0 + 64 + KT - 1) / KT);
+    if (CAUSAL) n_mine = min(n_mine, (wq0 + WQ + KT - 1) / KT);
 
     const size_t rs = (size_t)H * D64;  // elements between consecutive positions
     const bf16* qp = q + ((size_t)b * Lq * H + hh) * D64;
@@ -103,26 +129,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
     // wq0 + 32qb + l32, d = 16kk + 8half .. +7.  Rows past Lq read as zeros.
     const __amdgpu_buffer_rsrc_t qrsrc =
         make_rsrc(qp, (uint32_t)(((size_t)(Lq - 1) * rs + D64) * sizeof(bf16)));
-    bf16x8 qop[2][4];
+    bf16x8 qop[QB][4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const int qi = wq0 + 32 * qb + l32;
         const uint32_t qoff =
             qi < Lq ? (uint32_t)(((size_t)qi * rs + 8 * half) * sizeof(bf16)) : OOB_OFFSET;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
+        for (int kk = 0; kk < 4; ++kk) qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
     }
 
-    f32x16 acc[2][2];  // [query block][d block]
+    f32x16 acc[QB][2];  // [query block][d block]
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
-    float m_run[2] = {-INFINITY, -INFINITY};  // running max of the raw logits q.k
-    float l_part[2] = {0.0f, 0.0f};           // this lane's share of the row sum
+    float m_run[QB], l_part[QB];  // running max of the raw logits q.k; this lane's row-sum share
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = -INFINITY;
+        l_part[qb] = 0.0f;
+    }
 
     // Cooperative tile load: KT rows x 128 B of K and of V, 16 B per chunk,
     // through buffer resources that end at the last legal key row: rows at
@@ -138,39 +167,38 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
         voff[u] = (uint32_t)(((size_t)(c >> 3) * rs + (c & 7) * 8) * sizeof(bf16));
     }
     const uint32_t tile_bytes = (uint32_t)((size_t)KT * rs * sizeof(bf16));
-    bf16x8 kreg[CHUNKS], vreg[CHUNKS];
+    // Two register sets: loads run two tiles ahead of the LDS ring.
+    bf16x8 kreg[2][CHUNKS], vreg[2][CHUNKS];
     // Unconditional (branch-free) tile load; tiles at or past n_tiles read
     // zeros without touching memory.
-    auto gload = [&](int t) {
+    auto gload = [&](int set, int t) {
         const uint32_t base = t < n_tiles ? (uint32_t)t * tile_bytes : OOB_OFFSET;
 #pragma unroll
         for (int u = 0; u < CHUNKS; ++u) {
-            kreg[u] = buffer_load16(krsrc, base + voff[u]);
-            vreg[u] = buffer_load16(vrsrc, base + voff[u]);
+            kreg[set][u] = buffer_load16(krsrc, base + voff[u]);
+            vreg[set][u] = buffer_load16(vrsrc, base + voff[u]);
         }
     };
-    auto sstore = [&](int stage) {
+    auto sstore = [&](int set, int stage) {
 #pragma unroll
         for (int u = 0; u < CHUNKS; ++u) {
             const int c = tid + THREADS * u;
             const int off = stage * TILE + (c >> 3) * PITCH + (c & 7) * 8;
-            *(bf16x8*)(sK + off) = kreg[u];
-            *(bf16x8*)(sV + off) = vreg[u];
+            *(bf16x8*)(sK + off) = kreg[set][u];
+            *(bf16x8*)(sV + off) = vreg[set][u];
         }
     };
 
-    // S^T for one tile: S[qb] (32 keys x 32 queries) from the K tile in LDS.
-    auto scores = [&](int stage, f32x16 (&S)[2]) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[qb][r] = 0.0f;
+    const f32x16 zero16 = {};
+    // S^T for one tile (prologue only): S[qb] = K Q^T, 32 keys x 32 queries.
+    auto scores = [&](int stage, f32x16 (&S)[QB]) {
         const bf16* kt = sK + stage * TILE + l32 * PITCH + 8 * half;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const bf16x8 a = *(const bf16x8*)(kt + 16 * kk);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) S[qb] = mfma32(a, qop[qb][kk], S[qb]);
+            for (int qb = 0; qb < QB; ++qb)
+                S[qb] = mfma32(a, qop[qb][kk], kk == 0 ? zero16 : S[qb]);
         }
     };
 
@@ -180,12 +208,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
     // the exponent offset m_run is a stale maximum, so p = exp2((s - m) c)
     // stays below 2^8: the ratio acc / l is unaffected (softmax(x) =
     // softmax(x - c) for any c), and bf16/fp32 have range to spare.
-    auto mask_and_max = [&](int t, f32x16 (&S)[2]) {
+    auto mask_and_max = [&](int t, f32x16 (&S)[QB]) {
         const int k0 = t * KT;
         const bool need_mask = (k0 + KT > kv_end) || (CAUSAL && k0 + KT - 1 > wq0);
         if (need_mask) {
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < QB; ++qb) {
                 const int qi = wq0 + 32 * qb + l32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -197,7 +225,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
             }
         }
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             float mx = S[qb][0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[qb][r]);
@@ -224,8 +252,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
     // exp((s - m)/sqrt(d)), rounded to bf16 into the P operand; the row sum
     // accumulates the rounded p, the values PV actually uses.
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-    auto exp_pair = [&](const f32x16 (&S)[2], const float (&mc)[2], bf16x8 (&pop)[2][2], int qb,
-                        int i) {
+    auto exp_pair = [&](const f32x16 (&S)[QB], const float (&mc)[QB], bf16x8 (&pop)[QB][2],
+                        int qb, int i) {
         const int e = 2 * i;  // register index in S[qb]; chunk e/8, slot e%8
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][e], scale_log2e, -mc[qb]));
         const float p1 =
@@ -236,11 +264,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
         l_part[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part[qb], false);
     };
 
-    // One tile of the pipeline: S for tile j+1 and P_j V_j on the MFMA pipe,
-    // the exponentiation of tile j on the VALU, hand-interleaved one MFMA per
-    // two p values (sched_barrier fences keep the order).
-    const f32x16 zero16 = {};
-    auto tile_step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+    // One tile of the pipeline.  Slot s (0 .. 8*QB-1) issues one MFMA and
+    // exponentiates pair s (query block s/8, values 2(s%8), 2(s%8)+1).  The
+    // first 4*QB MFMAs are the scores of tile j+1; the rest are P_j V_j in
+    // (query block, chunk, d block) order, each issued once its P chunk is
+    // complete (chunk (qb, c) is done after pair 8qb + 4c + 3); those not
+    // ready by the last slot run after it.  sched_barrier fences keep the
+    // order.
+    auto tile_step = [&](int j, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
         // LDS operands, issued up front: K of tile j+1, V^T of tile j.  P
         // chunk c covers keys 16c + {0..3, 8..11} (k = 0..7, lanes < 32) and
         // 16c + {4..7, 12..15} (k = 8..15, lanes >= 32); the matching V^T
@@ -265,64 +296,69 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_d64(
         __builtin_amdgcn_sched_barrier(0);
 
         mask_and_max(j, Scur);
-        float mc[2];
+        float mc[QB];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
             mc[qb] = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb] * scale_log2e;
-        bf16x8 pop[2][2];  // P^T operands [query block][16-key chunk]
+        bf16x8 pop[QB][2];  // P^T operands [query block][16-key chunk]
 
-        // S_{j+1} (8 MFMAs) against the exponentials of query block 0.
+        // Raised priority while this wave feeds the MFMA pipe, so the
+        // arbiter favours a wave in its MFMA phase over one in its softmax
+        // or load phase.
+        __builtin_amdgcn_s_setprio(1);
+        constexpr int NS = 4 * QB;  // score MFMAs
+        constexpr int NSLOT = 8 * QB;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int s = 0; s < NSLOT; ++s) {
             __builtin_amdgcn_sched_barrier(0);
-            const int qb = i & 1, kk = i >> 1;
-            Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
-            exp_pair(Scur, mc, pop, 0, i);
-        }
-        // P_j V_j for query block 0, then block 1 as its chunks complete.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (i < 4) {
-                acc[0][i & 1] = mfma32(va[i >> 1][i & 1], pop[0][i >> 1], acc[0][i & 1]);
-            } else if (i < 6) {
-                acc[1][i & 1] = mfma32(va[0][i & 1], pop[1][0], acc[1][i & 1]);
+            if (s < NS) {
+                const int qb = s % QB, kk = s / QB;
+                Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
+            } else {
+                const int n = s - NS, qb = n / 4, c = (n / 2) % 2, db = n % 2;
+                if (s >= 8 * qb + 4 * c + 4) acc[qb][db] = mfma32(va[c][db], pop[qb][c], acc[qb][db]);
             }
-            exp_pair(Scur, mc, pop, 1, i);
+            exp_pair(Scur, mc, pop, s / 8, s % 8);
         }
         __builtin_amdgcn_sched_barrier(0);
-        acc[1][0] = mfma32(va[1][0], pop[1][1], acc[1][0]);
-        acc[1][1] = mfma32(va[1][1], pop[1][1], acc[1][1]);
+#pragma unroll
+        for (int n = 0; n < 4 * QB; ++n) {
+            const int s = NS + n, qb = n / 4, c = (n / 2) % 2, db = n % 2;
+            if (!(s >= 8 * qb + 4 * c + 4)) acc[qb][db] = mfma32(va[c][db], pop[qb][c], acc[qb][db]);
+        }
+        __builtin_amdgcn_s_setprio(0);
     };
 
-    // ---- prologue: tiles 0 and 1 into the ring, tile 2 into registers ----
-    gload(0);
-    sstore(0);
-    gload(1);
-    sstore(1);
-    gload(2);
+    // ---- prologue: tiles 0 and 1 into the ring, tiles 2 and 3 in flight ----
+    gload(0, 0);
+    sstore(0, 0);
+    gload(1, 1);
+    sstore(1, 1);
+    gload(0, 2);
+    gload(1, 3);
     __syncthreads();
 
-    f32x16 SA[2], SB[2];
+    f32x16 SA[QB], SB[QB];
     if (0 < n_mine) scores(0, SA);
 
-    // ---- main loop, unrolled by two so the score buffers alternate ----
-    auto iteration = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+    // ---- main loop, unrolled by two so the score buffers and the load
+    // register sets alternate ----
+    auto iteration = [&](int j, int set, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
         __syncthreads();  // tile j+1 is stored; everyone is done with tile j-1
-        sstore((j + 2) % STAGES);
-        gload(j + 3);
+        sstore(set, (j + 2) % STAGES);
+        gload(set, j + 4);
         // Past a wave's last tile, S_{j+1} reads a zero or unused stage and
         // is dropped.
         if (j < n_mine) tile_step(j, Scur, Snext);
     };
     for (int j = 0; j < n_tiles; j += 2) {
-        iteration(j, SA, SB);
-        if (j + 1 < n_tiles) iteration(j + 1, SB, SA);
+        iteration(j, 0, SA, SB);
+        if (j + 1 < n_tiles) iteration(j + 1, 1, SB, SA);
     }
 
     // ---- epilogue: O = acc / l, or 0 for a row with no legal key ----
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = sum_halves(l_part[qb]);
         const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
         const int qi = wq0 + 32 * qb + l32;
@@ -454,9 +490,9 @@ hipError_t launch_f32_d(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int NW>
-hipError_t launch_bf16_nw(const AttnArgs& a, hipStream_t stream) {
-    constexpr int BM = 64 * NW;
+template <int NW, int QB>
+hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
+    constexpr int BM = 32 * QB * NW;
     const int n_qtiles = (a.Lq + BM - 1) / BM;
     const dim3 grid((unsigned)((long)a.B * a.H * n_qtiles));
     const dim3 block(64 * NW);
@@ -467,20 +503,20 @@ hipError_t launch_bf16_nw(const AttnArgs& a, hipStream_t stream) {
     bf16* o = (bf16*)a.o;
     switch (a.mask) {
         case 0:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, false, false>), grid, block, 0, stream, q, k,
-                               v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, QB, false, false>), grid, block, 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         case 1:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, true, false>), grid, block, 0, stream, q, k,
-                               v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, QB, true, false>), grid, block, 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         case 2:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, false, true>), grid, block, 0, stream, q, k,
-                               v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, QB, false, true>), grid, block, 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         default:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, true, true>), grid, block, 0, stream, q, k,
-                               v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, QB, true, true>), grid, block, 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
     }
     return hipGetLastError();
@@ -489,8 +525,8 @@ hipError_t launch_bf16_nw(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
-    // Four waves (256 queries) per workgroup share each K/V tile.
-    return launch_bf16_nw<4>(a, stream);
+    // Four waves per workgroup share each K/V tile; each wave owns 32 queries.
+    return launch_bf16<ATTN_NW, ATTN_QB>(a, stream);
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {
