@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(2, 100, 77, 512, 8, 64), (1, 3, 130, 256, 4, 64),
-                                   (3, 129, 129, 1024, 16, 64)])
+                                   (3, 129, 129, 1024, 16, 64),
+                                   # many tiles: the launch with the 2-stage LDS ring
+                                   (64, 128, 128, 512, 8, 64), (40, 200, 150, 512, 8, 64)])
 def test_project_qkv(dtype, shape):
     dev = device()
     B, Lq, Lk, dm, h, d = shape

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
     sstore(1, 1);
     gload(0, 2);
     gload(1, 3);
-    __syncthreads();
+    barrier_lds();
 
     f32x16 SA[QB], SB[QB];
     if (0 < n_mine) scores(0, SA);
@@ -344,16 +344,18 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
     // ---- main loop, unrolled by two so the score buffers and the load
     // register sets alternate ----
     auto iteration = [&](int j, int set, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
-        __syncthreads();  // tile j+1 is stored; everyone is done with tile j-1
+        barrier_lds();  // tile j+1 is stored; everyone is done with tile j-1
         sstore(set, (j + 2) % STAGES);
         gload(set, j + 4);
         // Past a wave's last tile, S_{j+1} reads a zero or unused stage and
         // is dropped.
         if (j < n_mine) tile_step(j, Scur, Snext);
     };
+    // Both halves always run (an odd tail costs one barrier and loads that
+    // read zeros), so the load/store pattern is the same on every trip.
     for (int j = 0; j < n_tiles; j += 2) {
         iteration(j, 0, SA, SB);
-        if (j + 1 < n_tiles) iteration(j + 1, 1, SB, SA);
+        iteration(j + 1, 1, SB, SA);
     }
 
     // ---- epilogue: O = acc / l, or 0 for a row with no legal key ----

@@ -73,6 +73,37 @@ __device__ __forceinline__ bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Workgroup barrier for LDS hand-offs: each wave's LDS reads and writes
+// complete before it arrives, while its in-flight global loads (register
+// prefetches and direct-to-LDS loads) keep flying; callers wait for those
+// explicitly where needed.  The "memory" clobber stops the compiler from
+// moving memory accesses across it.  (__syncthreads() would also wait for
+// every outstanding global load.)
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct global-to-LDS load of 16 bytes per lane: lane i writes LDS bytes
+// lds_base + 16 i .. + 15 from byte offset voff of the buffer (zeros past
+// its end).  Issued as inline asm so the compiler adds no waits of its own
+// for it: the caller waits with s_waitcnt vmcnt before the data is read.
+// M0 carries the LDS base; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base,
+                                           uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base),
+                 "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// 32-bit LDS address of a __shared__ object.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(p);
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;
 #pragma unroll

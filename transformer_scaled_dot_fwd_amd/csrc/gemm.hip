@@ -18,39 +18,84 @@ namespace {
 
 struct GemmBatch {
     GemmProblem p[3];
+    int n_probs;
 };
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA GEMM.  Workgroup tile 128 (m) x 128 (n), k step 64; 4 waves in a
-// 2 x 2 arrangement, each owning 64 x 64 of the output as 2 x 2 blocks of
-// 32 x 32.  The kernel computes Y^T = W^T X^T so that an accumulator column
-// is one row m of Y and each lane stores 4 consecutive n (8 bytes):
+// bf16 MFMA GEMM.  4 waves in a 2 x 2 arrangement; wave (wm, wn) owns a
+// (32 TM) x (32 TN) block of the output as TM x TN accumulators of 32 x 32,
+// so the workgroup tile is BM = 64 TM rows by BN = 64 TN columns; k step 64.
+// The kernel computes Y^T = W^T X^T so that an accumulator column is one row
+// m of Y and each lane stores 4 consecutive n (8 bytes):
 //   A = W^T  (32 n x 16 k): LDS transpose reads of the row-major W tile
 //   B = X^T  (16 k x 32 m): 16-byte LDS reads of the row-major X tile
+// Operand tiles stream through a 3-stage LDS ring filled by direct
+// global-to-LDS buffer loads (lane i of a load writes LDS bytes
+// base + 16i .. base + 16i + 15), two k steps ahead of the MFMAs.  Both
+// tiles are stored with their 16-byte chunks XOR-swizzled by row so the
+// row reads of X and the transpose reads of W hit distinct LDS banks.
 // ---------------------------------------------------------------------------
-constexpr int GBM = 128;
-constexpr int GBN = 128;
 constexpr int GBK = 64;
-constexpr int XS = GBK + 8;   // LDS pitch of the X tile [m][k], elements (144 B)
-constexpr int WS = GBN + 8;   // LDS pitch of the W tile [k][n], elements (272 B)
+constexpr int GSTAGES = 3;
 constexpr int GT = 256;
 
-__global__ __launch_bounds__(GT, 2) void gemm_bf16_kernel(GemmBatch batch, int N, int K) {
-    const GemmProblem P = batch.p[blockIdx.z];
-    const int M = P.M;
-    const int m0 = blockIdx.x * GBM;
-    if (m0 >= M) return;  // uniform across the workgroup, before any barrier
-    const int n0 = blockIdx.y * GBN;
-    const bf16* X = (const bf16*)P.x;
-    const bf16* W = (const bf16*)P.w;
-    bf16* Y = (bf16*)P.y;
+// X tile: row r holds 8 chunks of 16 B (k = 8c .. 8c+7) at chunk c ^ (r & 7).
+__device__ __forceinline__ int x_chunk(int r, int c) { return c ^ (r & 7); }
+// W tile: row k holds BN/8 chunks (n = 8c .. 8c+7) at chunk c ^ w_swz(k).
+__device__ __forceinline__ int w_swz(int k) { return (4 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }
 
-    __shared__ __attribute__((aligned(16))) bf16 sX[GBM * XS];
-    __shared__ __attribute__((aligned(16))) bf16 sW[GBK * WS];
+// s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int TM, int TN, int ST>
+__device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, int K, int n_mt,
+                                               int n_nt) {
+    constexpr int BM = 64 * TM;
+    constexpr int BN = 64 * TN;
+    constexpr int X_BYTES = BM * GBK * 2;          // one X stage
+    constexpr int W_BYTES = GBK * BN * 2;          // one W stage
+    constexpr int X_INSTR = X_BYTES / 1024 / 4;    // 1 KB loads per wave per stage
+    constexpr int W_INSTR = W_BYTES / 1024 / 4;
+    constexpr int W_ROW_CHUNKS = BN / 8;
+    constexpr int W_ROWS_PER_INSTR = 64 / W_ROW_CHUNKS;
+    static_assert(X_INSTR >= 1 && W_INSTR >= 1 && W_ROW_CHUNKS >= 16, "tile shape");
+
+    // Tile order.  Tiles are numbered m-tile major, then problem, then
+    // n-tile, so consecutive tiles share their X rows (the three projections
+    // of self-attention read the same X).  Workgroups are dispatched to the
+    // 8 XCDs round-robin (workgroup w on XCD w % 8); when the tile count
+    // divides by 8, XCD x runs the contiguous tile range x*T/8 .. so its L2
+    // keeps the X rows of the tiles in flight and the (small) weights.
+    const int n_pt = batch.n_probs * n_nt;
+    const int T = n_mt * n_pt;
+    const int w = (int)blockIdx.x;
+    const int t = (T & 7) == 0 ? (w & 7) * (T >> 3) + (w >> 3) : w;
+    const int mt = t / n_pt;
+    const int prob = (t % n_pt) / n_nt;
+    const int nt = t % n_nt;
+    const GemmProblem P = batch.p[prob];
+    const int M = P.M;
+    const int m0 = mt * BM;
+    if (m0 >= M) return;  // uniform across the workgroup, before any barrier
+    const int n0 = nt * BN;
+
+    static_assert(ST >= 2 && ST <= 4, "ring depth");
+    // One LDS allocation: the operand ring (ST X stages, then ST W stages),
+    // reused after the main loop for the output tile.
+    constexpr int OPITCH = 2 * BN + 16;  // output tile row pitch in bytes
+    constexpr int RING_BYTES = ST * (X_BYTES + W_BYTES);
+    constexpr int SMEM_BYTES = RING_BYTES > BM * OPITCH ? RING_BYTES : BM * OPITCH;
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+    auto sX = [&](int st) { return smem + st * X_BYTES; };
+    auto sW = [&](int st) { return smem + ST * X_BYTES + st * W_BYTES; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5;
     const int l32 = lane & 31;
     const int g = lane >> 4;
@@ -58,80 +103,160 @@ __global__ __launch_bounds__(GT, 2) void gemm_bf16_kernel(GemmBatch batch, int N
     const int wn = wave & 1;
     const int wm = wave >> 1;
 
-    f32x16 acc[2][2];
+    // Buffer resources: X rows m0 .. M-1, W columns n0 .. (rows past the end
+    // of W read as zeros; columns past N only feed outputs that are not
+    // stored).
+    const bf16* X = (const bf16*)P.x + (size_t)m0 * K;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)((size_t)(M - m0) * K * 2));
+    const bf16* W = (const bf16*)P.w + n0;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)(((size_t)K * N - n0) * 2));
+
+    // Per-lane source offsets of this wave's loads (k step 0), fixed per lane.
+    uint32_t xoff[X_INSTR], woff[W_INSTR];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int u = 0; u < X_INSTR; ++u) {
+        const int t = wave + 4 * u;           // 1 KB slice of the stage = 8 rows
+        const int r = 8 * t + (lane >> 3);
+        const int c = x_chunk(r, lane & 7);   // physical chunk lane&7 holds logical c
+        xoff[u] = (uint32_t)(((size_t)r * K + 8 * c) * 2);
+    }
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+    for (int u = 0; u < W_INSTR; ++u) {
+        const int t = wave + 4 * u;
+        const int r = W_ROWS_PER_INSTR * t + lane / W_ROW_CHUNKS;
+        const int c = (lane % W_ROW_CHUNKS) ^ w_swz(r);
+        woff[u] = (uint32_t)(((size_t)r * N + 8 * c) * 2);
+    }
+    auto issue = [&](int kt, int st) {  // direct loads of k step kt into stage st
+        const uint32_t xs = lds_addr(sX(st));
+        const uint32_t ws = lds_addr(sW(st));
+        const uint32_t xk = (uint32_t)kt * GBK * 2;
+        const uint32_t wk = (uint32_t)((size_t)kt * GBK * N * 2);
+#pragma unroll
+        for (int u = 0; u < X_INSTR; ++u)
+            load_lds16(xr, xs + (wave + 4 * u) * 1024, xoff[u] + xk);
+#pragma unroll
+        for (int u = 0; u < W_INSTR; ++u)
+            load_lds16(wr, ws + (wave + 4 * u) * 1024, woff[u] + wk);
+    };
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int c = 0; c < TM; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.0f;
 
-    bf16x8 xr[4], wr[4];
-    auto gload = [&](int k0) {
+    constexpr int PER_STAGE = X_INSTR + W_INSTR;
+    const int n_k = K / GBK;
+
+    // LDS operand reads of one 16-wide k slice of stage st.
+    auto read_ops = [&](int st, int k16, bf16x8 (&a)[TN], bf16x8 (&bx)[TM]) {
+        const char* xs = sX(st);
+        const char* ws = sW(st);
+        const int krow = 16 * k16 + 8 * (g >> 1) + (i16 >> 2);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = tid + GT * u;
-            const int xrow = c >> 3, xcol = (c & 7) * 8;
-            xr[u] = (m0 + xrow < M) ? *(const bf16x8*)(X + (size_t)(m0 + xrow) * K + k0 + xcol)
-                                    : zero_bf16x8();
-            const int wrow = c >> 4, wcol = (c & 15) * 8;
-            wr[u] = (n0 + wcol < N) ? *(const bf16x8*)(W + (size_t)(k0 + wrow) * N + n0 + wcol)
-                                    : zero_bf16x8();
+        for (int nb = 0; nb < TN; ++nb) {
+            const int n = 32 * TN * wn + 32 * nb + 16 * (g & 1) + 4 * (i16 & 3);
+            const int c = n >> 3, byte = (n & 7) * 2;
+            const bf16* lo =
+                (const bf16*)(ws + krow * (2 * BN) + ((c ^ w_swz(krow)) << 4) + byte);
+            const bf16* hi = (const bf16*)(ws + (krow + 4) * (2 * BN) +
+                                           ((c ^ w_swz(krow + 4)) << 4) + byte);
+            a[nb] = join(lds_read_tr(lo), lds_read_tr(hi));
+        }
+#pragma unroll
+        for (int mb = 0; mb < TM; ++mb) {
+            const int r = 32 * TM * wm + 32 * mb + l32;
+            bx[mb] = *(const bf16x8*)(xs + r * 128 + (x_chunk(r, 2 * k16 + half) << 4));
         }
     };
-    auto sstore = [&]() {
+    auto mfmas = [&](const bf16x8 (&a)[TN], const bf16x8 (&bx)[TM]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = tid + GT * u;
-            *(bf16x8*)(sX + (c >> 3) * XS + (c & 7) * 8) = xr[u];
-            *(bf16x8*)(sW + (c >> 4) * WS + (c & 15) * 8) = wr[u];
-        }
+        for (int nb = 0; nb < TN; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = mfma32(a[nb], bx[mb], acc[nb][mb]);
     };
 
-    const int n_k = K / GBK;
-    gload(0);
-    for (int kt = 0; kt < n_k; ++kt) {
-        __syncthreads();
-        sstore();
-        __syncthreads();
-        if (kt + 1 < n_k) gload((kt + 1) * GBK);
+    // One k step: wait for this wave's loads of step kt (up to ST-2 later
+    // steps may still fly), barrier (every wave's loads visible; the stage
+    // of step kt-1 is free), start step kt+ST-1 into that stage, then the
+    // four k slices with the operand reads of slice i+1 in flight while the
+    // MFMAs of slice i run.
+    bf16x8 opA[2][TN], opB[2][TM];
+    auto step = [&](int kt, int st) {
+        const int ahead = min(ST - 2, n_k - 1 - kt);
+        if (ahead >= 2) wait_vmcnt<2 * PER_STAGE>();
+        else if (ahead == 1) wait_vmcnt<PER_STAGE>();
+        else wait_vmcnt<0>();
+        barrier_lds();
+        if (kt + ST - 1 < n_k) issue(kt + ST - 1, (st + ST - 1) % ST);
+        read_ops(st, 0, opA[0], opB[0]);
 #pragma unroll
         for (int k16 = 0; k16 < GBK / 16; ++k16) {
-            bf16x8 a[2], bx[2];
-            const int krow = 16 * k16 + 8 * (g >> 1) + (i16 >> 2);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int col = 64 * wn + 32 * nb + 16 * (g & 1) + 4 * (i16 & 3);
-                a[nb] = join(lds_read_tr(sW + krow * WS + col),
-                             lds_read_tr(sW + (krow + 4) * WS + col));
-            }
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                bx[mb] = *(const bf16x8*)(sX + (64 * wm + 32 * mb + l32) * XS + 16 * k16 +
-                                          8 * half);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32(a[nb], bx[mb], acc[nb][mb]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (k16 + 1 < GBK / 16) read_ops(st, k16 + 1, opA[(k16 + 1) & 1], opB[(k16 + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(opA[k16 & 1], opB[k16 & 1]);
         }
-    }
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = m0 + 64 * wm + 32 * mb + l32;
-        if (m >= M) continue;
+    for (int s = 0; s < ST - 1; ++s)
+        if (s < n_k) issue(s, s);
+    for (int kt = 0; kt < n_k; kt += ST) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int s = 0; s < ST; ++s)
+            if (kt + s < n_k) step(kt + s, s);
+    }
+
+    // Epilogue: the output tile goes through LDS (reusing the operand ring)
+    // so that global stores are whole 16-byte chunks of contiguous row
+    // segments rather than 8-byte pieces scattered over 32 rows.  The pitch
+    // of 2*BN + 16 bytes spreads a column of 8-byte writes over the banks.
+    barrier_lds();  // every wave is done reading the operand ring
+    char* so = smem;
+#pragma unroll
+    for (int mb = 0; mb < TM; ++mb) {
+        const int r = 32 * TM * wm + 32 * mb + l32;
+#pragma unroll
+        for (int nb = 0; nb < TN; ++nb)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int n = n0 + 64 * wn + 32 * nb + 8 * rg + 4 * half;
-                if (n >= N) continue;
+                const int n = 32 * TN * wn + 32 * nb + 8 * rg + 4 * half;
                 bf16x4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) out[e] = (bf16)acc[nb][mb][4 * rg + e];
-                *(bf16x4*)(Y + (size_t)m * N + n) = out;
+                *(bf16x4*)(so + r * OPITCH + n * 2) = out;
             }
     }
+    barrier_lds();
+    bf16* Y = (bf16*)P.y;
+    constexpr int ROW_CHUNKS = BN / 8;  // 16-byte chunks per tile row
+#pragma unroll
+    for (int it = 0; it < BM * ROW_CHUNKS / GT; ++it) {
+        const int idx = tid + GT * it;
+        const int r = idx / ROW_CHUNKS, c = idx % ROW_CHUNKS;
+        const int m = m0 + r, n = n0 + 8 * c;
+        if (m < M && n < N)
+            *(bf16x8*)(Y + (size_t)m * N + n) = *(const bf16x8*)(so + r * OPITCH + c * 16);
+    }
+}
+
+// The two uses get their own kernel names so traces and counters tell them
+// apart.
+template <int TM, int TN, int ST>
+__global__ __launch_bounds__(GT, 2) void qkv_projection_gemm(GemmBatch batch, int N, int K,
+                                                             int n_mt, int n_nt) {
+    gemm_bf16_body<TM, TN, ST>(batch, N, K, n_mt, n_nt);
+}
+
+template <int TM, int TN, int ST>
+__global__ __launch_bounds__(GT, 2) void out_projection_gemm(GemmBatch batch, int N, int K,
+                                                             int n_mt, int n_nt) {
+    gemm_bf16_body<TM, TN, ST>(batch, N, K, n_mt, n_nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -189,6 +314,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmBatch batch, int N, i
 
 GemmBatch make_batch(const GemmProblem* probs, int n, int* max_m) {
     GemmBatch b{};
+    b.n_probs = n;
     *max_m = 0;
     for (int i = 0; i < n; ++i) {
         b.p[i] = probs[i];
@@ -199,14 +325,31 @@ GemmBatch make_batch(const GemmProblem* probs, int n, int* max_m) {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmProblem* probs, int n_probs, int N, int K,
+template <int TM, int TN, int ST>
+hipError_t launch_bf16_tiles(const GemmBatch& batch, int max_m, int N, int K, bool qkv,
+                             hipStream_t stream) {
+    const int n_mt = (max_m + 64 * TM - 1) / (64 * TM);
+    const int n_nt = (N + 64 * TN - 1) / (64 * TN);
+    const dim3 grid((unsigned)((long)n_mt * n_nt * batch.n_probs));
+    if (qkv)
+        hipLaunchKernelGGL((qkv_projection_gemm<TM, TN, ST>), grid, dim3(GT), 0, stream, batch, N,
+                           K, n_mt, n_nt);
+    else
+        hipLaunchKernelGGL((out_projection_gemm<TM, TN, ST>), grid, dim3(GT), 0, stream, batch, N,
+                           K, n_mt, n_nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(const GemmProblem* probs, int n_probs, int N, int K, bool qkv,
                             hipStream_t stream) {
     int max_m;
     const GemmBatch batch = make_batch(probs, n_probs, &max_m);
-    const dim3 grid((unsigned)((max_m + GBM - 1) / GBM), (unsigned)((N + GBN - 1) / GBN),
-                    (unsigned)n_probs);
-    hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(GT), 0, stream, batch, N, K);
-    return hipGetLastError();
+    // 128 x 128 tiles.  With more than two tiles per CU a 2-stage ring
+    // (64 KB of LDS) lets two workgroups share a CU; otherwise the 3-stage
+    // ring prefetches deeper for the single workgroup.
+    const long tiles = (long)((max_m + 127) / 128) * ((N + 127) / 128) * n_probs;
+    if (tiles > 512) return launch_bf16_tiles<2, 2, 2>(batch, max_m, N, K, qkv, stream);
+    return launch_bf16_tiles<2, 2, 3>(batch, max_m, N, K, qkv, stream);
 }
 
 hipError_t launch_gemm_f32(const GemmProblem* probs, int n_probs, int N, int K,

@@ -28,8 +28,9 @@ struct GemmProblem {
     int M;
 };
 
-// Up to three independent problems sharing N and K, in one launch.
-hipError_t launch_gemm_bf16(const GemmProblem* probs, int n_probs, int N, int K,
+// Up to three independent problems sharing N and K, in one launch; `qkv`
+// only selects the kernel's name (projection of Q/K/V vs. W^O).
+hipError_t launch_gemm_bf16(const GemmProblem* probs, int n_probs, int N, int K, bool qkv,
                             hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmProblem* probs, int n_probs, int N, int K,
                            hipStream_t stream);

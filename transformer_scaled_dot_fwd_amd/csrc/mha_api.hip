@@ -86,7 +86,7 @@ int mha_project_qkv(mha_dtype dt, int B, int Lq, int Lk, int d_model, int h, int
         probs[n++] = {x_kv, w_v, v, (int)Mkv};
     }
     const hipError_t e = (dt == MHA_BF16)
-                             ? mha::launch_gemm_bf16(probs, n, (int)N, d_model, stream)
+                             ? mha::launch_gemm_bf16(probs, n, (int)N, d_model, true, stream)
                              : mha::launch_gemm_f32(probs, n, (int)N, d_model, stream);
     return launch_status(e);
 }
@@ -104,7 +104,7 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model, const
         return MHA_ERR_UNSUPPORTED;
     mha::GemmProblem prob{o, w_o, y, (int)M};
     const hipError_t e = (dt == MHA_BF16)
-                             ? mha::launch_gemm_bf16(&prob, 1, d_model, (int)K, stream)
+                             ? mha::launch_gemm_bf16(&prob, 1, d_model, (int)K, false, stream)
                              : mha::launch_gemm_f32(&prob, 1, d_model, (int)K, stream);
     return launch_status(e);
 }
