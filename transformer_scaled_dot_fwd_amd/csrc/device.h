@@ -79,8 +79,15 @@ __device__ __forceinline__ bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32
 // explicitly where needed.  The "memory" clobber stops the compiler from
 // moving memory accesses across it.  (__syncthreads() would also wait for
 // every outstanding global load.)
+// The wait and the barrier are builtins so the compiler's own wait
+// bookkeeping sees every LDS read retired here; the empty asm statements
+// keep memory accesses on their side.
 __device__ __forceinline__ void barrier_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("" ::: "memory");
+    // s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained (gfx9 encoding)
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Direct global-to-LDS load of 16 bytes per lane: lane i writes LDS bytes

@@ -35,12 +35,16 @@ struct GemmBatch {
 // tiles are stored with their 16-byte chunks XOR-swizzled by row so the
 // row reads of X and the transpose reads of W hit distinct LDS banks.
 // ---------------------------------------------------------------------------
-constexpr int GBK = 64;
-constexpr int GSTAGES = 3;
 constexpr int GT = 256;
 
-// X tile: row r holds 8 chunks of 16 B (k = 8c .. 8c+7) at chunk c ^ (r & 7).
-__device__ __forceinline__ int x_chunk(int r, int c) { return c ^ (r & 7); }
+// X tile: row r holds BK/8 chunks of 16 B (k = 8c .. 8c+7), chunk c at
+// position c ^ x_swz(r), so that the 16-byte row reads of 8 consecutive rows
+// hit distinct banks: rows of 128 B (BK = 64) permute by r & 7, rows of 64 B
+// (BK = 32) by (r >> 1) & 3.
+template <int BK>
+__device__ __forceinline__ int x_chunk(int r, int c) {
+    return BK == 64 ? c ^ (r & 7) : c ^ ((r >> 1) & 3);
+}
 // W tile: row k holds BN/8 chunks (n = 8c .. 8c+7) at chunk c ^ w_swz(k).
 __device__ __forceinline__ int w_swz(int k) { return (4 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }
 
@@ -51,13 +55,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int TM, int TN, int ST>
+template <int TM, int TN, int ST, int BK>
 __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, int K, int n_mt,
                                                int n_nt) {
     constexpr int BM = 64 * TM;
     constexpr int BN = 64 * TN;
-    constexpr int X_BYTES = BM * GBK * 2;          // one X stage
-    constexpr int W_BYTES = GBK * BN * 2;          // one W stage
+    static_assert(BK == 32 || BK == 64, "k step");
+    constexpr int X_BYTES = BM * BK * 2;           // one X stage
+    constexpr int W_BYTES = BK * BN * 2;           // one W stage
+    constexpr int X_ROW_CHUNKS = BK / 8;           // 16-byte chunks per X row
+    constexpr int X_ROWS_PER_KB = 64 / X_ROW_CHUNKS;
     constexpr int X_INSTR = X_BYTES / 1024 / 4;    // 1 KB loads per wave per stage
     constexpr int W_INSTR = W_BYTES / 1024 / 4;
     constexpr int W_ROW_CHUNKS = BN / 8;
@@ -115,9 +122,9 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, in
     uint32_t xoff[X_INSTR], woff[W_INSTR];
 #pragma unroll
     for (int u = 0; u < X_INSTR; ++u) {
-        const int t = wave + 4 * u;           // 1 KB slice of the stage = 8 rows
-        const int r = 8 * t + (lane >> 3);
-        const int c = x_chunk(r, lane & 7);   // physical chunk lane&7 holds logical c
+        const int t = wave + 4 * u;           // 1 KB slice of the stage
+        const int r = X_ROWS_PER_KB * t + lane / X_ROW_CHUNKS;
+        const int c = x_chunk<BK>(r, lane % X_ROW_CHUNKS);  // logical chunk at this position
         xoff[u] = (uint32_t)(((size_t)r * K + 8 * c) * 2);
     }
 #pragma unroll
@@ -130,8 +137,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, in
     auto issue = [&](int kt, int st) {  // direct loads of k step kt into stage st
         const uint32_t xs = lds_addr(sX(st));
         const uint32_t ws = lds_addr(sW(st));
-        const uint32_t xk = (uint32_t)kt * GBK * 2;
-        const uint32_t wk = (uint32_t)((size_t)kt * GBK * N * 2);
+        const uint32_t xk = (uint32_t)kt * BK * 2;
+        const uint32_t wk = (uint32_t)((size_t)kt * BK * N * 2);
 #pragma unroll
         for (int u = 0; u < X_INSTR; ++u)
             load_lds16(xr, xs + (wave + 4 * u) * 1024, xoff[u] + xk);
@@ -149,7 +156,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, in
             for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.0f;
 
     constexpr int PER_STAGE = X_INSTR + W_INSTR;
-    const int n_k = K / GBK;
+    const int n_k = K / BK;
 
     // LDS operand reads of one 16-wide k slice of stage st.
     auto read_ops = [&](int st, int k16, bf16x8 (&a)[TN], bf16x8 (&bx)[TM]) {
@@ -169,7 +176,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, in
 #pragma unroll
         for (int mb = 0; mb < TM; ++mb) {
             const int r = 32 * TM * wm + 32 * mb + l32;
-            bx[mb] = *(const bf16x8*)(xs + r * 128 + (x_chunk(r, 2 * k16 + half) << 4));
+            bx[mb] = *(const bf16x8*)(xs + r * (2 * BK) + (x_chunk<BK>(r, 2 * k16 + half) << 4));
         }
     };
     auto mfmas = [&](const bf16x8 (&a)[TN], const bf16x8 (&bx)[TM]) {
@@ -194,9 +201,9 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, in
         if (kt + ST - 1 < n_k) issue(kt + ST - 1, (st + ST - 1) % ST);
         read_ops(st, 0, opA[0], opB[0]);
 #pragma unroll
-        for (int k16 = 0; k16 < GBK / 16; ++k16) {
+        for (int k16 = 0; k16 < BK / 16; ++k16) {
             __builtin_amdgcn_sched_barrier(0);
-            if (k16 + 1 < GBK / 16) read_ops(st, k16 + 1, opA[(k16 + 1) & 1], opB[(k16 + 1) & 1]);
+            if (k16 + 1 < BK / 16) read_ops(st, k16 + 1, opA[(k16 + 1) & 1], opB[(k16 + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
             mfmas(opA[k16 & 1], opB[k16 & 1]);
         }
@@ -247,16 +254,16 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, in
 
 // The two uses get their own kernel names so traces and counters tell them
 // apart.
-template <int TM, int TN, int ST>
-__global__ __launch_bounds__(GT, 2) void qkv_projection_gemm(GemmBatch batch, int N, int K,
-                                                             int n_mt, int n_nt) {
-    gemm_bf16_body<TM, TN, ST>(batch, N, K, n_mt, n_nt);
+template <int TM, int TN, int ST, int BK, int OCC>
+__global__ __launch_bounds__(GT, OCC) void qkv_projection_gemm(GemmBatch batch, int N, int K,
+                                                               int n_mt, int n_nt) {
+    gemm_bf16_body<TM, TN, ST, BK>(batch, N, K, n_mt, n_nt);
 }
 
-template <int TM, int TN, int ST>
-__global__ __launch_bounds__(GT, 2) void out_projection_gemm(GemmBatch batch, int N, int K,
-                                                             int n_mt, int n_nt) {
-    gemm_bf16_body<TM, TN, ST>(batch, N, K, n_mt, n_nt);
+template <int TM, int TN, int ST, int BK, int OCC>
+__global__ __launch_bounds__(GT, OCC) void out_projection_gemm(GemmBatch batch, int N, int K,
+                                                               int n_mt, int n_nt) {
+    gemm_bf16_body<TM, TN, ST, BK>(batch, N, K, n_mt, n_nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -325,18 +332,18 @@ GemmBatch make_batch(const GemmProblem* probs, int n, int* max_m) {
 
 }  // namespace
 
-template <int TM, int TN, int ST>
+template <int TM, int TN, int ST, int BK, int OCC>
 hipError_t launch_bf16_tiles(const GemmBatch& batch, int max_m, int N, int K, bool qkv,
                              hipStream_t stream) {
     const int n_mt = (max_m + 64 * TM - 1) / (64 * TM);
     const int n_nt = (N + 64 * TN - 1) / (64 * TN);
     const dim3 grid((unsigned)((long)n_mt * n_nt * batch.n_probs));
     if (qkv)
-        hipLaunchKernelGGL((qkv_projection_gemm<TM, TN, ST>), grid, dim3(GT), 0, stream, batch, N,
-                           K, n_mt, n_nt);
+        hipLaunchKernelGGL((qkv_projection_gemm<TM, TN, ST, BK, OCC>), grid, dim3(GT), 0, stream,
+                           batch, N, K, n_mt, n_nt);
     else
-        hipLaunchKernelGGL((out_projection_gemm<TM, TN, ST>), grid, dim3(GT), 0, stream, batch, N,
-                           K, n_mt, n_nt);
+        hipLaunchKernelGGL((out_projection_gemm<TM, TN, ST, BK, OCC>), grid, dim3(GT), 0, stream,
+                           batch, N, K, n_mt, n_nt);
     return hipGetLastError();
 }
 
@@ -344,12 +351,13 @@ hipError_t launch_gemm_bf16(const GemmProblem* probs, int n_probs, int N, int K,
                             hipStream_t stream) {
     int max_m;
     const GemmBatch batch = make_batch(probs, n_probs, &max_m);
-    // 128 x 128 tiles.  With more than two tiles per CU a 2-stage ring
-    // (64 KB of LDS) lets two workgroups share a CU; otherwise the 3-stage
-    // ring prefetches deeper for the single workgroup.
+    // 128 x 128 tiles.  With more than one tile per CU, a k step of 32 and a
+    // 3-stage ring (48 KB of LDS) let three workgroups share a CU, so up to
+    // 768 tiles run in a single round and hide each other's load latency;
+    // otherwise one workgroup per CU streams k steps of 64.
     const long tiles = (long)((max_m + 127) / 128) * ((N + 127) / 128) * n_probs;
-    if (tiles > 512) return launch_bf16_tiles<2, 2, 2>(batch, max_m, N, K, qkv, stream);
-    return launch_bf16_tiles<2, 2, 3>(batch, max_m, N, K, qkv, stream);
+    if (tiles > 256) return launch_bf16_tiles<2, 2, 3, 32, 3>(batch, max_m, N, K, qkv, stream);
+    return launch_bf16_tiles<2, 2, 3, 64, 2>(batch, max_m, N, K, qkv, stream);
 }
 
 hipError_t launch_gemm_f32(const GemmProblem* probs, int n_probs, int N, int K,
