@@ -40,9 +40,6 @@ namespace mha {
 // of tile j are interleaved, one MFMA per two exponentials, with the
 // softmax VALU work of tile j.  Global loads run two tiles ahead.
 // ---------------------------------------------------------------------------
-#ifndef ATTN_QB
-#define ATTN_QB 2
-#endif
 #ifndef ATTN_QB1_OCC
 #define ATTN_QB1_OCC 3
 #endif
@@ -527,8 +524,14 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
-    // Four waves per workgroup share each K/V tile; each wave owns 32 queries.
-    return launch_bf16<ATTN_NW, ATTN_QB>(a, stream);
+    // Four waves per workgroup share each K/V tile.  Short rows, and causal
+    // rows up to 2048, run 32 queries per wave: twice the workgroups and
+    // three per CU, which hides load latency and evens out the causal
+    // triangle.  Longer rows run 64 queries per wave, halving the LDS reads
+    // per MFMA.
+    const bool causal = (a.mask & 2) != 0;  // AttnArgs::mask bit 1
+    if (a.Lq <= 512 || (causal && a.Lq <= 2048)) return launch_bf16<ATTN_NW, 1>(a, stream);
+    return launch_bf16<ATTN_NW, 2>(a, stream);
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {
