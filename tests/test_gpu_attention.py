@@ -60,7 +60,8 @@ def test_fp32_ragged(d, mask):
 
 @pytest.mark.parametrize("mask", [NONE, PAD, CAUSAL, PAD | CAUSAL])
 @pytest.mark.parametrize("shape", [(3, 2, 200, 177), (2, 3, 64, 64), (1, 1, 1, 1),
-                                   (2, 2, 5, 300), (1, 2, 257, 257)])
+                                   (2, 2, 5, 300), (1, 2, 257, 257), (2, 2, 333, 96),
+                                   (2, 3, 129, 256), (1, 2, 100, 33)])
 def test_bf16_ragged(shape, mask):
     dev = device()
     B, h, Lq, Lk = shape
@@ -117,14 +118,17 @@ def test_named_workload_sampled(name):
 # Properties that hold at any size (bit-exact where the method fixes bits).
 # ---------------------------------------------------------------------------
 
+# Lengths on both sides of 256 keys: rows of at most 256 keys run the
+# whole-row-in-LDS kernel, longer rows the streaming one.
+@pytest.mark.parametrize("L", [150, 300])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_padding_garbage_is_never_read(dtype):
+def test_padding_garbage_is_never_read(dtype, L):
     """Rows of K/V at or beyond the length may hold anything (NaN, Inf,
     1e30): O is bit-identical to the run with zeros there."""
     dev = device()
-    B, h, L, d = 4, 2, 150, 64
+    B, h, d = 4, 2, 64
     q, k, v = make(B, h, L, L, d, dtype, 901)
-    lens = torch.tensor([150, 3, 64, 100], dtype=torch.int32)
+    lens = torch.tensor([L, 3, 64, L - 50], dtype=torch.int32)
     k0, v0 = k.clone(), v.clone()
     for b in range(B):
         k0[b, lens[b]:] = 0
@@ -140,12 +144,13 @@ def test_padding_garbage_is_never_read(dtype):
             assert torch.equal(o2, base), (dtype, mask, junk)
 
 
-def test_causal_prefix_is_unaffected_by_later_keys():
+@pytest.mark.parametrize("L", [200, 300])
+def test_causal_prefix_is_unaffected_by_later_keys(L):
     dev = device()
-    B, h, L, d = 2, 2, 300, 64
+    B, h, d = 2, 2, 64
     q, k, v = make(B, h, L, L, d, "bf16", 902)
     base = run(q, k, v, CAUSAL, None, dev)
-    for t in (0, 63, 64, 200):
+    for t in (0, 63, 64, 130, L - 20):
         k2, v2 = k.clone(), v.clone()
         k2[:, t + 1:] = generate.normal(k2[:, t + 1:].shape, 903 + t, "bf16") * 50
         v2[:, t + 1:] = generate.normal(v2[:, t + 1:].shape, 904 + t, "bf16") * 50
@@ -153,13 +158,14 @@ def test_causal_prefix_is_unaffected_by_later_keys():
         assert torch.equal(o2[:, :t + 1], base[:, :t + 1]), t
 
 
+@pytest.mark.parametrize("L", [70, 290])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_single_key_and_empty_rows(dtype):
+def test_single_key_and_empty_rows(dtype, L):
     """One legal key: O is that V row bit-exactly; no legal key: O = 0."""
     dev = device()
-    B, h, L, d = 3, 2, 70, 64
+    B, h, d = 3, 2, 64
     q, k, v = make(B, h, L, L, d, dtype, 905)
-    lens = torch.tensor([1, 0, 70], dtype=torch.int32)
+    lens = torch.tensor([1, 0, L], dtype=torch.int32)
     o = run(q, k, v, PAD, lens, dev).cpu()
     assert torch.equal(o[0], v[0, 0:1].expand(L, h, d))
     assert torch.equal(o[1], torch.zeros(L, h, d, dtype=o.dtype))
@@ -178,13 +184,14 @@ def test_empty_and_keyless_calls():
     assert torch.equal(o.cpu(), torch.zeros(2, 8, 2, 64, dtype=torch.bfloat16))
 
 
-def test_uniform_and_constant_values():
+@pytest.mark.parametrize("L", [190, 400])
+def test_uniform_and_constant_values(L):
     """K = 0: every logit equal, O_i = mean of the legal V rows.
     V = 1: O = 1 (weights sum to one)."""
     dev = device()
-    B, h, L, d = 2, 2, 190, 64
+    B, h, d = 2, 2, 64
     q, k, v = make(B, h, L, L, d, "bf16", 908)
-    lens = torch.tensor([190, 77], dtype=torch.int32)
+    lens = torch.tensor([L, 77], dtype=torch.int32)
     kz = torch.zeros_like(k)
     for mask in (PAD, CAUSAL | PAD):
         o = run(q, kz, v, mask, lens, dev)
@@ -194,11 +201,12 @@ def test_uniform_and_constant_values():
         assert torch.equal(o1.cpu(), torch.ones_like(o1.cpu()))
 
 
-def test_shift_invariance_large_logits():
+@pytest.mark.parametrize("L", [256, 320])
+def test_shift_invariance_large_logits(L):
     """Adding u to every key shifts each logit row by q.u/8: the output is
     unchanged within tolerance and stays finite for shifts of ~1e3."""
     dev = device()
-    B, h, L, d = 2, 2, 256, 64
+    B, h, d = 2, 2, 64
     q, k, v = make(B, h, L, L, d, "bf16", 909)
     u = torch.full((1, 1, h, d), 16.0, dtype=torch.bfloat16)   # exact in bf16
     for mask in (NONE, CAUSAL):

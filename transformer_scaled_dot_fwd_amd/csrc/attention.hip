@@ -327,9 +327,9 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
     };
 
     // ---- prologue: tiles 0 and 1 into the ring, tiles 2 and 3 in flight ----
-    gload(0, 0);
-    sstore(0, 0);
+    gload(0, 0);  // tiles 0 and 1 in flight together: one round trip
     gload(1, 1);
+    sstore(0, 0);
     sstore(1, 1);
     gload(0, 2);
     gload(1, 3);
@@ -373,6 +373,236 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
                     *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * half) = out;
                 }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, d = 64, rows of at most 256 keys (8 tiles): every K/V row of the
+// (batch row, head) fits in LDS, so it is loaded at once.
+//
+// Workgroup = 4 waves = one (batch row, head, block of 128 queries); wave w
+// owns 32 consecutive queries, one per lane column.  All K/V tiles go to
+// LDS by direct global-to-LDS loads issued together (one memory round trip)
+// behind a single barrier; each wave then runs its tiles with no further
+// synchronisation: S^T = K Q^T (4 MFMAs), mask, online softmax as above,
+// O^T += V^T P^T (4 MFMAs).  The output block is staged through LDS so that
+// each 128-byte (query, head) row is written whole.
+//
+// LDS tiles here are 32 rows of 128 bytes without padding (a direct load
+// writes 16 contiguous bytes per lane); the eight 16-byte chunks of a row
+// are permuted by row so both read patterns spread over the banks:
+//   K (16-byte row reads):               chunk c of row r at c ^ (r & 7)
+//   V (transpose reads of 8 rows x 64 B): chunk c of row r at c ^ 4((r >> 1) & 1)
+// ---------------------------------------------------------------------------
+constexpr int SHORT_TILE_BYTES = KT * D64 * 2;  // one K (or V) tile
+constexpr int SHORT_BM = 128;                   // queries per workgroup
+
+__device__ __forceinline__ constexpr int k_swz(int r) { return r & 7; }
+__device__ __forceinline__ constexpr int v_swz(int r) { return 4 * ((r >> 1) & 1); }
+
+template <int NT, bool PAD, bool CAUSAL>
+__global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
+    int n_qtiles, float scale_log2e) {
+    static_assert(NT >= 4 && 2 * NT * SHORT_TILE_BYTES >= 4 * 32 * 128, "LDS for the output");
+    __shared__ __attribute__((aligned(1024))) char smem[NT * 2 * SHORT_TILE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+
+    // Tile decode: as for long rows (all query blocks of a (batch row, head)
+    // on one XCD; causal: longest blocks first).
+    const int nbh = B * H;
+    const int w = (int)blockIdx.x;
+    int bh, qt;
+    if ((nbh & 7) == 0) {
+        const int x = w & 7, slot = w >> 3, per = nbh >> 3;
+        if (CAUSAL) {
+            qt = n_qtiles - 1 - slot / per;
+            bh = x * per + slot % per;
+        } else {
+            bh = x * per + slot / n_qtiles;
+            qt = slot % n_qtiles;
+        }
+    } else if (CAUSAL) {
+        qt = n_qtiles - 1 - w / nbh;
+        bh = w % nbh;
+    } else {
+        bh = w / n_qtiles;
+        qt = w % n_qtiles;
+    }
+    const int b = bh / H;
+    const int hh = bh - b * H;
+    const int q0 = qt * SHORT_BM;
+
+    int kv_end = Lk;
+    if (PAD) kv_end = min(max(kv_lens[b], 0), Lk);
+    int key_end = kv_end;
+    if (CAUSAL) key_end = min(key_end, min(q0 + SHORT_BM, Lq));
+    const int n_tiles = (key_end + KT - 1) / KT;  // <= NT: Lk <= 32 NT
+    const int wq0 = q0 + 32 * wave;
+    int n_mine = (wq0 < Lq) ? n_tiles : 0;
+    if (CAUSAL) n_mine = min(n_mine, (wq0 + 32 + KT - 1) / KT);
+
+    const size_t rs = (size_t)H * D64;
+    const uint32_t rsb = (uint32_t)(rs * sizeof(bf16));
+    const bf16* qp = q + ((size_t)b * Lq * H + hh) * D64;
+    const bf16* kp = k + ((size_t)b * Lk * H + hh) * D64;
+    const bf16* vp = v + ((size_t)b * Lk * H + hh) * D64;
+    bf16* op = o + ((size_t)b * Lq * H + hh) * D64;
+
+    // Q (B operand of S^T = K Q^T): lane holds query wq0 + l32, d = 16kk +
+    // 8half .. +7.  Rows past Lq read as zeros.
+    const __amdgpu_buffer_rsrc_t qrsrc =
+        make_rsrc(qp, (uint32_t)(((size_t)(Lq - 1) * rs + D64) * sizeof(bf16)));
+    bf16x8 qop[4];
+    {
+        const int qi = wq0 + l32;
+        const uint32_t qoff = qi < Lq ? (uint32_t)qi * rsb + 16 * half : OOB_OFFSET;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qop[kk] = buffer_load16(qrsrc, qoff + 32 * kk);
+    }
+
+    // Every K/V tile of the row into LDS: thread tid fills chunk position
+    // tid of tile t's K and V (row tid / 8); rows at or past kv_end land as
+    // zeros without a memory access.
+    {
+        const uint32_t kv_bytes = kv_end > 0 ? (uint32_t)(kv_end - 1) * rsb + D64 * 2 : 0u;
+        const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kp, kv_bytes);
+        const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vp, kv_bytes);
+        const int pr = tid >> 3, pc = tid & 7;
+        const uint32_t k_dma = (uint32_t)pr * rsb + 16 * (pc ^ k_swz(pr));
+        const uint32_t v_dma = (uint32_t)pr * rsb + 16 * (pc ^ v_swz(pr));
+        const uint32_t tile_gbytes = (uint32_t)KT * rsb;
+        const uint32_t lds_wave = lds_addr(smem) + 1024 * wave;
+        for (int t = 0; t < n_tiles; ++t) {
+            const uint32_t st = lds_wave + (uint32_t)t * 2 * SHORT_TILE_BYTES;
+            load_lds16(krsrc, st, (uint32_t)t * tile_gbytes + k_dma);
+            load_lds16(vrsrc, st + SHORT_TILE_BYTES, (uint32_t)t * tile_gbytes + v_dma);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));  // vmcnt(0)
+    barrier_lds();
+
+    // LDS operand reads (same lane patterns as the long-row kernel).
+    uint32_t k_rd[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = l32 * 128 + 16 * ((2 * kk + half) ^ k_swz(l32));
+    uint32_t v_rd[2];
+    {
+        const int row = 4 * half + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            const int chunk = 4 * db + 2 * (g & 1) + ((i16 & 3) >> 1);
+            v_rd[db] = row * 128 + 16 * (chunk ^ v_swz(row)) + 8 * (i16 & 1);
+        }
+    }
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    float m_run = -INFINITY, l_part = 0.0f;
+    const f32x16 zero16 = {};
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+    for (int t = 0; t < n_mine; ++t) {
+        const char* kb = smem + t * 2 * SHORT_TILE_BYTES;
+        const char* vb = kb + SHORT_TILE_BYTES;
+        bf16x8 ka[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[kk] = *(const bf16x8*)(kb + k_rd[kk]);
+        bf16x8 va[2][2];  // [16-key chunk][d block]
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+                va[c][db] = join(lds_read_tr((const bf16*)(vb + 2048 * c + v_rd[db])),
+                                 lds_read_tr((const bf16*)(vb + 2048 * c + v_rd[db] + 1024)));
+        f32x16 S = mfma32(ka[0], qop[0], zero16);
+#pragma unroll
+        for (int kk = 1; kk < 4; ++kk) S = mfma32(ka[kk], qop[kk], S);
+
+        // Mask the boundary tiles: key k0 + acc_row(r, half) is legal iff
+        // acc_row(r, 0) < lim.
+        const int k0 = t * KT;
+        if ((k0 + KT > kv_end) || (CAUSAL && k0 + KT - 1 > wq0)) {
+            int lim = kv_end - k0;
+            if (CAUSAL) lim = min(lim, wq0 + l32 + 1 - k0);
+            lim -= 4 * half;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = acc_row(r, 0) < lim ? S[r] : -INFINITY;
+        }
+
+        // Running maximum with the lazy rescale of the long-row kernel.
+        float mx = S[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        mx = max_halves(mx);
+        const bool grow = (mx - m_run) * scale_log2e > 8.0f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e) : 1.0f;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            l_part *= alpha;
+            m_run = m_new;
+        }
+        const float mc = (m_run == -INFINITY) ? 0.0f : m_run * scale_log2e;
+
+        // p = exp2(s c - m c), rounded to bf16 for PV; the row sum adds the
+        // rounded pairs.
+        bf16x8 pop[2];
+#pragma unroll
+        for (int pr2 = 0; pr2 < 8; ++pr2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * pr2], scale_log2e, -mc));
+            const float p1 =
+                __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * pr2 + 1], scale_log2e, -mc));
+            const bf16x2 pp = {(bf16)p0, (bf16)p1};
+            pop[pr2 >> 2][2 * (pr2 & 3)] = pp[0];
+            pop[pr2 >> 2][2 * (pr2 & 3) + 1] = pp[1];
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part, false);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < 2; ++db) acc[db] = mfma32(va[c][db], pop[c], acc[db]);
+    }
+
+    // Epilogue: O = acc / l (0 for a row with no legal key), staged in LDS
+    // (wave w: rows of its 32 queries, 128 B each, chunks permuted by row)
+    // and written back as whole rows, 16 bytes per lane.
+    barrier_lds();  // every wave is done with the K/V tiles
+    const float l_tot = sum_halves(l_part);
+    const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+    char* stg = smem + wave * 32 * 128;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            bf16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[db][4 * rg + e] * inv);
+            const int chunk = (4 * db + rg) ^ (l32 & 7);
+            *(bf16x4*)(stg + l32 * 128 + 16 * chunk + 8 * half) = out;
+        }
+    barrier_lds();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        const int qi = wq0 + r;
+        if (qi < Lq)
+            *(bf16x8*)(op + (size_t)qi * rs + 8 * c) =
+                *(const bf16x8*)(stg + r * 128 + 16 * (c ^ (r & 7)));
     }
 }
 
@@ -521,6 +751,36 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int NT>
+hipError_t launch_short_bf16(const AttnArgs& a, hipStream_t stream) {
+    const int n_qtiles = (a.Lq + SHORT_BM - 1) / SHORT_BM;
+    const dim3 grid((unsigned)((long)a.B * a.H * n_qtiles));
+    const float sl2e = (float)(1.4426950408889634 / sqrt((double)a.D));
+    const bf16* q = (const bf16*)a.q;
+    const bf16* k = (const bf16*)a.k;
+    const bf16* v = (const bf16*)a.v;
+    bf16* o = (bf16*)a.o;
+    switch (a.mask) {
+        case 0:
+            hipLaunchKernelGGL((attn_short_bf16_d64<NT, false, false>), grid, dim3(256), 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            break;
+        case 1:
+            hipLaunchKernelGGL((attn_short_bf16_d64<NT, true, false>), grid, dim3(256), 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            break;
+        case 2:
+            hipLaunchKernelGGL((attn_short_bf16_d64<NT, false, true>), grid, dim3(256), 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            break;
+        default:
+            hipLaunchKernelGGL((attn_short_bf16_d64<NT, true, true>), grid, dim3(256), 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
@@ -529,6 +789,9 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     // three per CU, which hides load latency and evens out the causal
     // triangle.  Longer rows run 64 queries per wave, halving the LDS reads
     // per MFMA.
+    // Rows of at most 128 (256) keys: the whole K/V row in LDS at once.
+    if (a.Lk <= 128) return launch_short_bf16<4>(a, stream);
+    if (a.Lk <= 256) return launch_short_bf16<8>(a, stream);
     const bool causal = (a.mask & 2) != 0;  // AttnArgs::mask bit 1
     if (a.Lq <= 512 || (causal && a.Lq <= 2048)) return launch_bf16<ATTN_NW, 1>(a, stream);
     return launch_bf16<ATTN_NW, 2>(a, stream);
