@@ -4,10 +4,12 @@
     python bench.py [--steps K] [--warmup W] [--workload c3] [--gpus 1]
 
 One step is one pass of the whole hot path over one batch of seeded synthetic
-input: the Q/K/V projection, the fused masked attention and the W^O
-projection (the base decoder block by default: X [64, 128, 512], h = 8,
-d_k = 64, causal + key padding).  Each step is a replay of a HIP graph that
-holds the three launches; K steps run back to back, bracketed by
+input: the Q/K/V projection, the masked attention and the W^O projection
+(the base decoder block by default: X [64, 128, 512], h = 8, d_k = 64,
+causal + key padding).  Where the self-attention rows are at most 128
+tokens long, the projection and the attention run as one fused kernel (two
+launches per step; ``--unfused`` keeps three).  Each step is a replay of a
+HIP graph that holds the launches; K steps run back to back, bracketed by
 torch.cuda.synchronize() and HIP events on the stream the kernels run on, and
 cycle over enough copies of every buffer that the 256 MB Infinity Cache
 cannot serve a repeat.
@@ -42,6 +44,8 @@ ROTATE_BYTES = 1 << 30        # rotate buffers over >= 1 GiB (Infinity Cache is 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "attention": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc", "attention.hip"),
+    "self_attention_fused": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc",
+                                         "fused.hip"),
     "project_qkv": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc", "gemm.hip"),
     "out_proj": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc", "gemm.hip"),
 }
@@ -69,7 +73,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough CPU-time budget of the oracle sample")
-    ap.add_argument("--kernel-only", choices=["project_qkv", "attention", "out_proj", "copy"])
+    ap.add_argument("--kernel-only", choices=["project_qkv", "attention", "out_proj",
+                                              "self_attention_fused", "copy"])
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as three launches (projection, attention, W^O) even "
+                         "where the fused self-attention kernel applies")
     return ap.parse_args()
 
 
@@ -90,6 +98,7 @@ class Block:
             s["o"] = torch.empty_like(s["q"])
             s["y"] = torch.empty((B, L, dm), dtype=torch.bfloat16, device=dev)
             self.sets.append(s)
+        self.fused = False
 
     def project_qkv(self, s):
         self.mha.mha_project_qkv(s["x"], s["x"], s["w_q"], s["w_k"], s["w_v"], self.w.h,
@@ -102,9 +111,20 @@ class Block:
     def out_proj(self, s):
         self.mha.mha_out_proj(s["o"], s["w_o"], out=s["y"])
 
+    def self_attention_fused(self, s):
+        return self.mha.mha_self_attention_fused(s["x"], s["w_q"], s["w_k"], s["w_v"],
+                                                 self.w.h, mask=self.w.mask,
+                                                 kv_lens=s["kv_lens"], out=s["o"])
+
+    def fused_supported(self):
+        return self.self_attention_fused(self.sets[0]) is not None
+
     def step(self, s):
-        self.project_qkv(s)
-        self.attention(s)
+        if self.fused:
+            self.self_attention_fused(s)
+        else:
+            self.project_qkv(s)
+            self.attention(s)
         self.out_proj(s)
 
 
@@ -281,11 +301,13 @@ def main():
     n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / one)))
     del probe
     blk = Block(w, inputs, dev, n_sets)
-    log(f"workload {w.name}: working set {one / 1e6:.1f} MB x {n_sets} rotating sets")
+    blk.fused = (not args.unfused) and blk.fused_supported()
+    log(f"workload {w.name}: working set {one / 1e6:.1f} MB x {n_sets} rotating sets; "
+        f"{'fused self-attention + W^O' if blk.fused else 'projection + attention + W^O'}")
 
     if args.kernel_only:
         fns = {"project_qkv": blk.project_qkv, "attention": blk.attention,
-               "out_proj": blk.out_proj}
+               "out_proj": blk.out_proj, "self_attention_fused": blk.self_attention_fused}
         if args.kernel_only == "copy":
             src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
             dst = torch.empty_like(src)
@@ -307,13 +329,18 @@ def main():
     value = flops_step / sec_step / 1e12
     log(f"step: {sec_step * 1e6:.2f} us, {value:.1f} TFLOP/s")
 
-    # ---- per-kernel durations, each timed alone in the same rotation ----
+    # ---- per-kernel durations, each timed alone in the same rotation: the
+    # kernels of the step, then (for reference) those of the other path ----
+    step_kernels = (["self_attention_fused", "out_proj"] if blk.fused
+                    else ["project_qkv", "attention", "out_proj"])
+    names = step_kernels + (["project_qkv", "attention"] if blk.fused else [])
     per = {}
-    for name in ("project_qkv", "attention", "out_proj"):
+    for name in names:
         fn = getattr(blk, name)
         per[name] = kernel_time(fn, blk.sets, max(args.steps, 2 * n_sets), args.warmup)
-        log(f"  {name}: {per[name] * 1e6:.2f} us")
-    dom = max(per, key=per.get)
+        log(f"  {name}: {per[name] * 1e6:.2f} us"
+            + ("" if name in step_kernels else " (not in the step)"))
+    dom = max(step_kernels, key=per.get)
     if dom == "attention":
         bound, alg, unit, peak = "hbm", work["attention"]["bytes"], "GB/s", PEAK_HBM_BYTES
     else:
@@ -330,7 +357,7 @@ def main():
         f = work[name]["flops"]
         b = work[name]["bytes"]
         kernels[name] = {"us": round(sec * 1e6, 3), "tflops": round(f / sec / 1e12, 1),
-                         "gbps": round(b / sec / 1e9, 1)}
+                         "gbps": round(b / sec / 1e9, 1), "in_step": name in step_kernels}
 
     sweep = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup)
     cpu = None
@@ -352,8 +379,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs, N(0,1/512) weights, lengths U{32..128})",
         "config": {"workload": w.name, "B": w.B, "L": w.Lq, "d_model": w.d_model, "h": w.h,
-                   "d_k": w.d, "mask": "causal+key_padding", "step": "project_qkv -> "
-                   "attention -> out_proj (HIP graph replay)", "rotating_sets": n_sets,
+                   "d_k": w.d, "mask": "causal+key_padding",
+                   "step": " -> ".join(step_kernels) + " (HIP graph replay)",
+                   "rotating_sets": n_sets,
                    "flops_per_step": flops_step},
         "frac_peak_bf16": round(value * 1e12 / PEAK_BF16_FLOPS, 4),
         "kernels": kernels,

@@ -137,6 +137,34 @@ int mha_project_qkv(mha_dtype dt, int B, int Lq, int Lk, int d_model, int h,
 int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
                  const void* o, const void* w_o, void* y, hipStream_t stream);
 
+/*
+ * mha_self_attention_fused -- the Q/K/V projections and the attention of
+ * every head of a self-attention layer in one launch, for rows of at most
+ * 128 tokens:
+ *
+ *     O = Concat_t softmax((X W_t^Q)(X W_t^K)^T / sqrt(d_k) + M) (X W_t^V)
+ *
+ * ([Slides] slide "Multi-Head Attention"; [Deep] section 04, attention
+ * equation with M and MultiHead equations).  The result equals
+ * mha_project_qkv(x, x, ...) followed by mha_forward(...) on the same
+ * arguments; the projected Q, K, V are never written to memory.
+ *
+ *   x          [B, L, d_model]         the layer input (queries and keys/values)
+ *   w_q, w_k, w_v [d_model, h*d_k]     row-vector convention, head t in column
+ *                                      block t
+ *   mask_flags, kv_lens                as for mha_forward (with Lq = Lk = L)
+ *   o          [B, L, h, d_k]  BLHD    output (the concat of the heads); must
+ *                                      not overlap the inputs
+ *
+ * Supported: MHA_BF16, d_k = 64, 1 <= L <= 128, d_model % 64 == 0, B*h <
+ * 2^31 (B == 0 is a no-op); MHA_ERR_UNSUPPORTED otherwise, in which case
+ * the two-call path computes the same thing.
+ */
+int mha_self_attention_fused(mha_dtype dt, int B, int L, int d_model, int h, int d_k,
+                             const void* x, const void* w_q, const void* w_k, const void* w_v,
+                             int mask_flags, const int32_t* kv_lens, void* o,
+                             hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* mha_status_string(int status);
 

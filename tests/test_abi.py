@@ -33,7 +33,7 @@ def L():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"mha_forward", "mha_project_qkv", "mha_out_proj",
-                                         "mha_status_string"}
+                                         "mha_self_attention_fused", "mha_status_string"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -98,6 +98,30 @@ def test_project_and_out_proj_validation(L):
     assert O(BF16, 2, 8, 8, 64, 500, FAKE, FAKE, FAKE, None) == UNSUPPORTED
     assert O(BF16, 0, 8, 8, 64, 512, FAKE, FAKE, FAKE, None) == OK
     assert O(9, 2, 8, 8, 64, 512, FAKE, FAKE, FAKE, None) == INVALID
+
+
+def test_fused_validation(L):
+    F = L.mha_self_attention_fused
+    # (dt, B, L, d_model, h, dk, x, wq, wk, wv, mask, lens, o, stream)
+    base = [BF16, 2, 128, 512, 8, 64] + [FAKE] * 4 + [0, None, FAKE, None]
+    keys = ["dt", "B", "L", "dm", "h", "dk", "x", "wq", "wk", "wv", "mask", "lens", "o"]
+    def call(**over):
+        a = list(base)
+        for name, val in over.items():
+            a[keys.index(name)] = val
+        return F(*a)
+    assert call(dt=5) == INVALID
+    assert call(L=0) == INVALID
+    assert call(h=0) == INVALID
+    assert call(mask=8) == INVALID
+    assert call(mask=1) == INVALID                  # key padding needs lengths
+    assert call(x=None) == INVALID
+    assert call(wk=FAKE + 2) == INVALID             # misaligned
+    assert call(L=129) == UNSUPPORTED               # rows of at most 128 tokens
+    assert call(dk=32) == UNSUPPORTED
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(dm=96) == UNSUPPORTED
+    assert call(B=0) == OK
 
 
 def test_python_binding_checks_before_calling():

@@ -87,3 +87,77 @@ def test_cross_attention_block():
     torch.cuda.synchronize()
     ref = oracle.mha_block(x, z, *ws, h=h, mask=1, kv_lens=lens)
     check(y, ref, "bf16", "cross-attention block")
+
+
+# ---------------------------------------------------------------------------
+# Self-attention with the projections fused in (rows of at most 128 tokens).
+# ---------------------------------------------------------------------------
+
+def _fused_inputs(B, L, dm, h, seed):
+    x = generate.normal((B, L, dm), seed, "bf16")
+    ws = [generate.normal((dm, h * 64), seed + 1 + i, "bf16", std=dm ** -0.5) for i in range(3)]
+    choices = [L, 1, 0, L + 7, max(L // 2, 1), -3, L - 1]
+    lens = torch.tensor([choices[i % len(choices)] for i in range(B)], dtype=torch.int32)
+    return x, ws, lens
+
+
+@pytest.mark.parametrize("mask", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape", [(64, 128, 512, 8), (3, 77, 512, 8), (2, 1, 256, 4),
+                                   (5, 100, 1024, 16), (2, 128, 64, 1), (9, 33, 128, 2)])
+def test_fused_self_attention_equals_two_call_path(shape, mask):
+    """The fused kernel does the projection GEMM's and the short-row
+    attention's arithmetic in the same order: identical bits."""
+    dev = device()
+    B, L, dm, h = shape
+    say(f"case fused {shape} mask={mask}")
+    x, ws, lens = _fused_inputs(B, L, dm, h, 1500 + L + dm + h + mask)
+    x, ws, lens = x.to(dev), [w.to(dev) for w in ws], lens.to(dev)
+    fused = mha.mha_self_attention_fused(x, *ws, h=h, mask=mask, kv_lens=lens)
+    assert fused is not None
+    q, k, v = mha.mha_project_qkv(x, x, *ws, h=h)
+    ref = mha.mha_forward(q, k, v, mask=mask, kv_lens=lens)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.cpu(), ref.cpu())
+
+
+@pytest.mark.parametrize("mask", [1, 3])
+def test_fused_self_attention_against_oracle(mask):
+    dev = device()
+    B, L, dm, h = 6, 120, 512, 8
+    say(f"case fused vs oracle mask={mask}")
+    x, ws, lens = _fused_inputs(B, L, dm, h, 1600 + mask)
+    o = mha.mha_self_attention_fused(x.to(dev), *(w.to(dev) for w in ws), h=h, mask=mask,
+                                     kv_lens=lens.to(dev))
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.project_qkv(x, x, *ws, h=h)
+    ref = oracle.attention(rq, rk, rv, mask=mask, kv_lens=lens)
+    check(o, ref, "bf16", f"fused self-attention m={mask}")
+
+
+def test_fused_padding_rows_of_x_are_not_read_as_keys():
+    """NaN/Inf in X at positions >= len_b: the K/V rows they project to are
+    masked and never reach the other rows' outputs."""
+    dev = device()
+    B, L, dm, h = 4, 96, 256, 4
+    x, ws, _ = _fused_inputs(B, L, dm, h, 1700)
+    lens = torch.tensor([96, 40, 1, 0], dtype=torch.int32)
+    wd = [w.to(dev) for w in ws]
+    base = mha.mha_self_attention_fused(x.to(dev), *wd, h=h, mask=1, kv_lens=lens.to(dev))
+    for junk in (float("nan"), float("inf")):
+        x2 = x.clone()
+        for b in range(B):
+            x2[b, lens[b]:] = junk
+        o2 = mha.mha_self_attention_fused(x2.to(dev), *wd, h=h, mask=1, kv_lens=lens.to(dev))
+        torch.cuda.synchronize()
+        for b in range(B):
+            n = int(lens[b])
+            assert torch.equal(o2[b, :n].cpu(), base[b, :n].cpu()), (junk, b)
+
+
+def test_fused_self_attention_unsupported_shapes():
+    dev = device()
+    x = generate.normal((2, 129, 256), 1800, "bf16").to(dev)
+    ws = [generate.normal((256, 4 * 64), 1801 + i, "bf16").to(dev) for i in range(3)]
+    assert mha.mha_self_attention_fused(x, *ws, h=4) is None           # L > 128
+    ws32 = [generate.normal((256, 8 * 32), 1811 + i, "bf16").to(dev) for i in range(3)]
+    assert mha.mha_self_attention_fused(x[:, :64].contiguous(), *ws32, h=8) is None  # d_k = 32

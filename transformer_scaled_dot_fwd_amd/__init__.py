@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.mha_project_qkv.restype = i
     L.mha_out_proj.argtypes = [i, i, i, i, i, i, p, p, p, p]
     L.mha_out_proj.restype = i
+    L.mha_self_attention_fused.argtypes = [i, i, i, i, i, i, p, p, p, p, i, p, p, p]
+    L.mha_self_attention_fused.restype = i
     L.mha_status_string.argtypes = [i]
     L.mha_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -186,9 +188,54 @@ def mha_out_proj(o: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor | None = 
     return out
 
 
+def mha_self_attention_fused(x: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                             w_v: torch.Tensor, h: int, mask: int = MASK_NONE,
+                             kv_lens: torch.Tensor | None = None,
+                             out: torch.Tensor | None = None) -> torch.Tensor | None:
+    """Self-attention of every head with the Q/K/V projections fused in:
+    x [B,L,d_model], w_* [d_model, h*64] -> o [B,L,h,64] (BLHD).  Returns
+    None when the shape is outside the fused kernel (bf16, d_k = 64,
+    L <= 128, d_model % 64 == 0): use the two-call path then."""
+    for t, n in ((x, "x"), (w_q, "w_q"), (w_k, "w_k"), (w_v, "w_v")):
+        _check(t, n, x.dtype)
+    B, L, dm = x.shape
+    nq = w_q.shape[1]
+    if w_q.shape != (dm, nq) or w_k.shape != (dm, nq) or w_v.shape != (dm, nq) or nq % h:
+        raise ValueError("weight shape mismatch")
+    dk = nq // h
+    lens_ptr = None
+    if mask & MASK_KEY_PADDING:
+        if kv_lens is None:
+            raise ValueError("key padding needs kv_lens")
+        _check(kv_lens, "kv_lens", torch.int32)
+        if kv_lens.shape != (B,):
+            raise ValueError(f"kv_lens must have shape ({B},)")
+        lens_ptr = kv_lens.data_ptr()
+    if out is None:
+        out = torch.empty((B, L, h, dk), dtype=x.dtype, device=x.device)
+    else:
+        _check(out, "out", x.dtype)
+        if out.shape != (B, L, h, dk):
+            raise ValueError("out has the wrong shape")
+    rc = lib().mha_self_attention_fused(_dtype_code(x), B, L, dm, h, dk, x.data_ptr(),
+                                        w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
+                                        int(mask), lens_ptr, out.data_ptr(), _stream(x.device))
+    if rc == 2:  # MHA_ERR_UNSUPPORTED
+        return None
+    if rc != 0:
+        raise MHAError(rc, "mha_self_attention_fused")
+    return out
+
+
 def mha_block(x_q, x_kv, w_q, w_k, w_v, w_o, h: int, mask: int = MASK_NONE, kv_lens=None):
-    """MultiHead(X_q, X_kv, X_kv) = Concat(head_1..head_h) W^O: three launches
-    on the current stream, no host synchronisation."""
-    q, k, v = mha_project_qkv(x_q, x_kv, w_q, w_k, w_v, h)
-    o = mha_forward(q, k, v, mask=mask, kv_lens=kv_lens)
+    """MultiHead(X_q, X_kv, X_kv) = Concat(head_1..head_h) W^O on the current
+    stream, no host synchronisation: for self-attention rows of at most 128
+    tokens, the fused projection + attention kernel and the W^O GEMM (two
+    launches); otherwise projection, attention and W^O (three launches)."""
+    o = None
+    if x_q is x_kv:
+        o = mha_self_attention_fused(x_q, w_q, w_k, w_v, h, mask=mask, kv_lens=kv_lens)
+    if o is None:
+        q, k, v = mha_project_qkv(x_q, x_kv, w_q, w_k, w_v, h)
+        o = mha_forward(q, k, v, mask=mask, kv_lens=kv_lens)
     return mha_out_proj(o, w_o)

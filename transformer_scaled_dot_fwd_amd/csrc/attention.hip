@@ -397,9 +397,6 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
 constexpr int SHORT_TILE_BYTES = KT * D64 * 2;  // one K (or V) tile
 constexpr int SHORT_BM = 128;                   // queries per workgroup
 
-__device__ __forceinline__ constexpr int k_swz(int r) { return r & 7; }
-__device__ __forceinline__ constexpr int v_swz(int r) { return 4 * ((r >> 1) & 1); }
-
 template <int NT, bool PAD, bool CAUSAL>
 __global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -487,7 +484,7 @@ __global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
             load_lds16(vrsrc, st + SHORT_TILE_BYTES, (uint32_t)t * tile_gbytes + v_dma);
         }
     }
-    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));  // vmcnt(0)
+    wait_vmcnt<0>();
     barrier_lds();
 
     // LDS operand reads (same lane patterns as the long-row kernel).

@@ -76,12 +76,11 @@ __device__ __forceinline__ bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32
 // Workgroup barrier for LDS hand-offs: each wave's LDS reads and writes
 // complete before it arrives, while its in-flight global loads (register
 // prefetches and direct-to-LDS loads) keep flying; callers wait for those
-// explicitly where needed.  The "memory" clobber stops the compiler from
-// moving memory accesses across it.  (__syncthreads() would also wait for
-// every outstanding global load.)
-// The wait and the barrier are builtins so the compiler's own wait
-// bookkeeping sees every LDS read retired here; the empty asm statements
-// keep memory accesses on their side.
+// explicitly where needed (__syncthreads() would also wait for every
+// outstanding global load).  The wait and the barrier are builtins so the
+// compiler's own wait bookkeeping sees every LDS read retired here; the
+// empty asm statements with "memory" clobbers keep memory accesses on their
+// side.
 __device__ __forceinline__ void barrier_lds() {
     asm volatile("" ::: "memory");
     // s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained (gfx9 encoding)
@@ -109,6 +108,22 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t
 template <typename T>
 __device__ __forceinline__ uint32_t lds_addr(T* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(p);
+}
+
+// Unpadded LDS tiles of 128-byte rows (what a direct global-to-LDS load
+// writes): the eight 16-byte chunks of row r are permuted so that both read
+// patterns spread over the banks.
+//   Row-read tiles (16-byte reads, one row per lane): chunk c at c ^ (r & 7).
+//   Transpose-read tiles (ds_read_b64_tr_b16 over 8 rows x 64 bytes): chunk c
+//   at c ^ 4((r >> 1) & 1).
+__device__ __forceinline__ constexpr int k_swz(int r) { return r & 7; }
+__device__ __forceinline__ constexpr int v_swz(int r) { return 4 * ((r >> 1) & 1); }
+
+// s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {

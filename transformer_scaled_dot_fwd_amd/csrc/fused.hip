@@ -1,0 +1,344 @@
+// fused.hip -- the self-attention of one (batch row, head) in one kernel,
+// for rows of at most 128 tokens:
+//
+//   [Q | K | V] = X_b [W_t^Q | W_t^K | W_t^V]        (L x 192, kept in LDS)
+//   O_t = softmax(Q K^T / sqrt(d_k) + M) V           (written, BLHD)
+//
+// ("Attention Is All You Need -- A Revolutionary Architecture for Sequence
+// Transduction", slide "Multi-Head Attention": head_i = Attention(Q W_i^Q,
+// K W_i^K, V W_i^V); "Paper Deep Reading", section 04, attention equation
+// with the mask M and the MultiHead equations.)  The projected Q, K and V
+// of a head never reach HBM: the projection's accumulators are rounded to
+// bf16 straight into the LDS tiles the attention reads.  The arithmetic is
+// that of the projection GEMM followed by the short-row attention kernel,
+// in the same order, so the output equals that of the two-kernel path.
+#include "device.h"
+#include "launch.h"
+
+namespace mha {
+namespace {
+
+constexpr int FL = 128;                               // rows (tokens) per batch row, at most
+constexpr int FKT = 32;                               // keys per attention tile
+constexpr int FBK = 32;                               // k step of the projection
+constexpr int FST = 3;                                // projection ring depth
+constexpr int FX_BYTES = FL * FBK * 2;                // X stage: 128 rows of 64 bytes
+constexpr int FW_MAT = FBK * 64 * 2;                  // one weight slab: 32 rows of 128 bytes
+constexpr int FW_BYTES = 3 * FW_MAT;                  // W stage: the head's slabs of W^Q, W^K, W^V
+constexpr int FRING = FST * (FX_BYTES + FW_BYTES);    // 60 KB
+constexpr int FTILE = FL * 64 * 2;                    // one of Q, K, V in LDS: 16 KB
+constexpr int FSMEM = FRING > 3 * FTILE ? FRING : 3 * FTILE;
+constexpr int F_PER_STAGE = 2 + 3;                    // direct loads per wave per stage
+
+// X stage: row r holds 4 chunks of 16 bytes (k = 8c .. 8c+7) at c ^ ((r >> 1) & 3).
+__device__ __forceinline__ int fx_chunk(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+template <bool PAD, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
+    const bf16* __restrict__ x, const bf16* __restrict__ wq, const bf16* __restrict__ wk,
+    const bf16* __restrict__ wv, const int32_t* __restrict__ kv_lens, bf16* __restrict__ o,
+    int B, int L, int DM, int H, float scale_log2e) {
+    __shared__ __attribute__((aligned(1024))) char smem[FSMEM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+
+    // Workgroup -> (batch row, head).  Workgroups are dispatched to the 8
+    // XCDs round-robin (workgroup w on XCD w % 8); when B*H divides by 8,
+    // XCD x gets the pairs x*nbh/8 .. (x+1)*nbh/8 - 1, so the heads of a
+    // batch row share one L2 for X_b.
+    const int nbh = B * H;
+    const int w = (int)blockIdx.x;
+    const int bh = (nbh & 7) == 0 ? (w & 7) * (nbh >> 3) + (w >> 3) : w;
+    const int b = bh / H;
+    const int hh = bh - b * H;
+    const int N = H * 64;  // row length of each weight matrix
+
+    // ---- projection: D^T = W^T X^T, 192 features x 128 tokens ----
+    // Wave (wm, wn) owns tokens 64 wm .. +63 (two 32-blocks) and features
+    // 96 wn .. +95 (three 32-blocks: feature block f lies in matrix f / 2).
+    const int wm = wave >> 1, wn = wave & 1;
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(x + (size_t)b * L * DM, (uint32_t)((size_t)L * DM * 2));
+    const bf16* wbase[3] = {wq + hh * 64, wk + hh * 64, wv + hh * 64};
+    const uint32_t w_bytes = (uint32_t)(((size_t)(DM - 1) * N + 64) * 2);
+    // Direct loads: X stage = 8 slices of 1 KB (16 rows of 64 bytes), wave
+    // w loads slices w and w + 4; W stage = 3 slabs of 4 KB, wave w loads
+    // rows 8w .. 8w+7 of each.
+    uint32_t xoff[2], woff;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r = 16 * (wave + 4 * u) + (lane >> 2);
+        xoff[u] = (uint32_t)(r * DM + 8 * fx_chunk(r, lane & 3)) * 2;
+    }
+    {
+        const int r = 8 * wave + (lane >> 3);
+        woff = (uint32_t)(r * N + 8 * ((lane & 7) ^ v_swz(r))) * 2;
+    }
+    auto sX = [&](int st) { return smem + st * FX_BYTES; };
+    auto sW = [&](int st) { return smem + FST * FX_BYTES + st * FW_BYTES; };
+    auto issue = [&](int kt, int st) {
+        const uint32_t xs = lds_addr(sX(st)), ws = lds_addr(sW(st));
+        const uint32_t xk = (uint32_t)kt * FBK * 2;
+        const uint32_t wk_ = (uint32_t)((size_t)kt * FBK * N * 2);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) load_lds16(xr, xs + (wave + 4 * u) * 1024, xoff[u] + xk);
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+            load_lds16(make_rsrc(wbase[u], w_bytes), ws + u * FW_MAT + wave * 1024, woff + wk_);
+    };
+
+    f32x16 acc[3][2];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][mb][r] = 0.0f;
+
+    // Operands of one 16-wide k slice.  A = W^T (32 features x 16 k) by
+    // transpose reads of the weight slab; B = X^T (16 k x 32 tokens) by
+    // 16-byte reads of the X stage.
+    auto read_ops = [&](int st, int k16, bf16x8 (&a)[3], bf16x8 (&bx)[2]) {
+        const char* ws = sW(st);
+        const char* xs = sX(st);
+        const int krow = 16 * k16 + 8 * (g >> 1) + (i16 >> 2);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int fb = 3 * wn + j;  // feature block 0..5
+            const char* slab = ws + (fb >> 1) * FW_MAT;
+            const int n = 32 * (fb & 1) + 16 * (g & 1) + 4 * (i16 & 3);
+            const int c = n >> 3, byte = (n & 7) * 2;
+            const bf16* lo = (const bf16*)(slab + krow * 128 + ((c ^ v_swz(krow)) << 4) + byte);
+            const bf16* hi =
+                (const bf16*)(slab + (krow + 4) * 128 + ((c ^ v_swz(krow + 4)) << 4) + byte);
+            a[j] = join(lds_read_tr(lo), lds_read_tr(hi));
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int r = 64 * wm + 32 * mb + l32;
+            bx[mb] = *(const bf16x8*)(xs + r * 64 + (fx_chunk(r, 2 * k16 + half) << 4));
+        }
+    };
+    const int n_k = DM / FBK;
+    bf16x8 opA[2][3], opB[2][2];
+    auto step = [&](int kt, int st) {
+        const int ahead = min(FST - 2, n_k - 1 - kt);
+        if (ahead >= 1) wait_vmcnt<F_PER_STAGE>();
+        else wait_vmcnt<0>();
+        barrier_lds();  // step kt visible everywhere; the stage of step kt-1 is free
+        if (kt + FST - 1 < n_k) issue(kt + FST - 1, (st + FST - 1) % FST);
+        read_ops(st, 0, opA[0], opB[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_ops(st, 1, opA[1], opB[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k16 = 0; k16 < 2; ++k16) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                    acc[j][mb] = mfma32(opA[k16][j], opB[k16][mb], acc[j][mb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < FST - 1; ++s)
+        if (s < n_k) issue(s, s);
+    for (int kt = 0; kt < n_k; kt += FST) {
+#pragma unroll
+        for (int s = 0; s < FST; ++s)
+            if (kt + s < n_k) step(kt + s, s);
+    }
+
+    // ---- Q, K, V to LDS as bf16, in the layouts the attention reads ----
+    // Register group q (r = 4q .. 4q+3) of feature block fb holds features
+    // 32 (fb & 1) + 8q + 4 half .. +3 of matrix fb / 2 for this lane's token.
+    // K and V rows at or past the row's length are stored as zeros: like
+    // the rows the attention kernels never load, whatever X holds there
+    // cannot reach the output.
+    int kv_end = L;
+    if (PAD) kv_end = min(max(kv_lens[b], 0), L);
+    barrier_lds();  // every wave is done with the projection ring
+    char* const sQ = smem;
+    char* const sK = smem + FTILE;
+    char* const sV = smem + 2 * FTILE;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int fb = 3 * wn + j;
+        const int mat = fb >> 1;
+        char* const dst = mat == 0 ? sQ : (mat == 1 ? sK : sV);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int m = 64 * wm + 32 * mb + l32;
+            const int swz = mat == 2 ? v_swz(m) : k_swz(m);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v4[e] = (mat == 0 || m < kv_end) ? (bf16)acc[j][mb][4 * q4 + e] : (bf16)0.0f;
+                const int chunk = 4 * (fb & 1) + q4;
+                *(bf16x4*)(dst + m * 128 + ((chunk ^ swz) << 4) + 8 * half) = v4;
+            }
+        }
+    }
+    barrier_lds();
+
+    // ---- attention: wave w owns queries 32w .. 32w+31, one per lane ----
+    const int n_tiles = (kv_end + FKT - 1) / FKT;
+    const int wq0 = 32 * wave;
+    int n_mine = (wq0 < L) ? n_tiles : 0;
+    if (CAUSAL) n_mine = min(n_mine, wave + 1);
+
+    bf16x8 qop[4];
+    {
+        const int r = wq0 + l32;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qop[kk] = *(const bf16x8*)(sQ + r * 128 + (((2 * kk + half) ^ k_swz(r)) << 4));
+    }
+    uint32_t k_rd[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = l32 * 128 + 16 * ((2 * kk + half) ^ k_swz(l32));
+    uint32_t v_rd[2];
+    {
+        const int row = 4 * half + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            const int chunk = 4 * db + 2 * (g & 1) + ((i16 & 3) >> 1);
+            v_rd[db] = row * 128 + 16 * (chunk ^ v_swz(row)) + 8 * (i16 & 1);
+        }
+    }
+    f32x16 oacc[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float m_run = -INFINITY, l_part = 0.0f;
+    const f32x16 zero16 = {};
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+    for (int t = 0; t < n_mine; ++t) {
+        const char* kb = sK + t * FKT * 128;
+        const char* vb = sV + t * FKT * 128;
+        bf16x8 ka[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[kk] = *(const bf16x8*)(kb + k_rd[kk]);
+        bf16x8 va[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+                va[c][db] = join(lds_read_tr((const bf16*)(vb + 2048 * c + v_rd[db])),
+                                 lds_read_tr((const bf16*)(vb + 2048 * c + v_rd[db] + 1024)));
+        f32x16 S = mfma32(ka[0], qop[0], zero16);
+#pragma unroll
+        for (int kk = 1; kk < 4; ++kk) S = mfma32(ka[kk], qop[kk], S);
+
+        const int k0 = t * FKT;
+        if ((k0 + FKT > kv_end) || (CAUSAL && k0 + FKT - 1 > wq0)) {
+            int lim = kv_end - k0;
+            if (CAUSAL) lim = min(lim, wq0 + l32 + 1 - k0);
+            lim -= 4 * half;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = acc_row(r, 0) < lim ? S[r] : -INFINITY;
+        }
+        float mx = S[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        mx = max_halves(mx);
+        const bool grow = (mx - m_run) * scale_log2e > 8.0f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e) : 1.0f;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            l_part *= alpha;
+            m_run = m_new;
+        }
+        const float mc = (m_run == -INFINITY) ? 0.0f : m_run * scale_log2e;
+        bf16x8 pop[2];
+#pragma unroll
+        for (int pr = 0; pr < 8; ++pr) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * pr], scale_log2e, -mc));
+            const float p1 =
+                __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * pr + 1], scale_log2e, -mc));
+            const bf16x2 pp = {(bf16)p0, (bf16)p1};
+            pop[pr >> 2][2 * (pr & 3)] = pp[0];
+            pop[pr >> 2][2 * (pr & 3) + 1] = pp[1];
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part, false);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < 2; ++db) oacc[db] = mfma32(va[c][db], pop[c], oacc[db]);
+    }
+
+    // ---- O = acc / l (0 without a legal key), staged over this wave's Q
+    // rows (read above by this wave only) and written as whole rows ----
+    const float l_tot = sum_halves(l_part);
+    const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+    char* stg = sQ + wq0 * 128;
+    barrier_lds();  // every lane of every wave holds its Q operands
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            bf16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (bf16)(oacc[db][4 * rg + e] * inv);
+            const int chunk = (4 * db + rg) ^ (l32 & 7);
+            *(bf16x4*)(stg + l32 * 128 + 16 * chunk + 8 * half) = out;
+        }
+    barrier_lds();
+    bf16* op = o + ((size_t)b * L * H + hh) * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        const int qi = wq0 + r;
+        if (qi < L)
+            *(bf16x8*)(op + (size_t)qi * N + 8 * c) =
+                *(const bf16x8*)(stg + r * 128 + 16 * (c ^ (r & 7)));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_self_attention_fused_bf16(const FusedArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((long)a.B * a.H));
+    const float sl2e = (float)(1.4426950408889634 / sqrt(64.0));
+    const bf16* x = (const bf16*)a.x;
+    const bf16* wq = (const bf16*)a.w_q;
+    const bf16* wk = (const bf16*)a.w_k;
+    const bf16* wv = (const bf16*)a.w_v;
+    bf16* o = (bf16*)a.o;
+    switch (a.mask) {
+        case 0:
+            hipLaunchKernelGGL((self_attention_fused_bf16<false, false>), grid, dim3(256), 0, stream,
+                               x, wq, wk, wv, a.kv_lens, o, a.B, a.L, a.DM, a.H, sl2e);
+            break;
+        case 1:
+            hipLaunchKernelGGL((self_attention_fused_bf16<true, false>), grid, dim3(256), 0, stream,
+                               x, wq, wk, wv, a.kv_lens, o, a.B, a.L, a.DM, a.H, sl2e);
+            break;
+        case 2:
+            hipLaunchKernelGGL((self_attention_fused_bf16<false, true>), grid, dim3(256), 0, stream,
+                               x, wq, wk, wv, a.kv_lens, o, a.B, a.L, a.DM, a.H, sl2e);
+            break;
+        default:
+            hipLaunchKernelGGL((self_attention_fused_bf16<true, true>), grid, dim3(256), 0, stream,
+                               x, wq, wk, wv, a.kv_lens, o, a.B, a.L, a.DM, a.H, sl2e);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mha

@@ -48,12 +48,6 @@ __device__ __forceinline__ int x_chunk(int r, int c) {
 // W tile: row k holds BN/8 chunks (n = 8c .. 8c+7) at chunk c ^ w_swz(k).
 __device__ __forceinline__ int w_swz(int k) { return (4 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }
 
-// s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int TM, int TN, int ST, int BK>
 __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, int K, int n_mt,
@@ -357,7 +351,7 @@ hipError_t launch_gemm_bf16(const GemmProblem* probs, int n_probs, int N, int K,
     // otherwise one workgroup per CU streams k steps of 64.
     const long tiles = (long)((max_m + 127) / 128) * ((N + 127) / 128) * n_probs;
     if (tiles > 256) return launch_bf16_tiles<2, 2, 3, 32, 3>(batch, max_m, N, K, qkv, stream);
-    return launch_bf16_tiles<2, 2, 3, 64, 2>(batch, max_m, N, K, qkv, stream);
+    return launch_bf16_tiles<2, 2, 3, 64, 1>(batch, max_m, N, K, qkv, stream);
 }
 
 hipError_t launch_gemm_f32(const GemmProblem* probs, int n_probs, int N, int K,

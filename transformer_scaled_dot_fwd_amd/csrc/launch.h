@@ -18,6 +18,20 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+
+// Self-attention of every (batch row, head) with the projections fused in:
+// x [B, L, DM], w_q/w_k/w_v [DM, H*64], o [B, L, H, 64]; L <= 128.
+struct FusedArgs {
+    int B, L, DM, H;
+    int mask;                 // bit 0: key padding, bit 1: causal
+    const void* x;
+    const void* w_q;
+    const void* w_k;
+    const void* w_v;
+    const int32_t* kv_lens;   // device, [B]; only read with key padding
+    void* o;
+};
+hipError_t launch_self_attention_fused_bf16(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 
 // One GEMM problem Y[M, N] = X[M, K] W[K, N] (row-major).

@@ -109,4 +109,27 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model, const
     return launch_status(e);
 }
 
+int mha_self_attention_fused(mha_dtype dt, int B, int L, int d_model, int h, int d_k,
+                             const void* x, const void* w_q, const void* w_k, const void* w_v,
+                             int mask_flags, const int32_t* kv_lens, void* o,
+                             hipStream_t stream) {
+    if (dt != MHA_F32 && dt != MHA_BF16) return MHA_ERR_INVALID_ARG;
+    if (B < 0 || L < 1 || d_model < 1 || h < 1 || d_k < 1) return MHA_ERR_INVALID_ARG;
+    if (mask_flags & ~(MHA_MASK_KEY_PADDING | MHA_MASK_CAUSAL)) return MHA_ERR_INVALID_ARG;
+    if (B == 0) return MHA_OK;
+    if (!x || !w_q || !w_k || !w_v || !o) return MHA_ERR_INVALID_ARG;
+    if ((mask_flags & MHA_MASK_KEY_PADDING) && !kv_lens) return MHA_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, w_q, w_k, w_v, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MHA_ERR_INVALID_ARG;
+    if (dt != MHA_BF16 || d_k != 64 || L > 128 || d_model % 64 != 0) return MHA_ERR_UNSUPPORTED;
+    if ((long long)B * h > INT_MAX || (long long)h * 64 > INT_MAX / 2) return MHA_ERR_UNSUPPORTED;
+    // One batch row of X and one weight matrix are addressed with 32-bit
+    // byte offsets.
+    if ((long long)L * d_model * 2 >= (1LL << 31) || (long long)d_model * h * 64 * 2 >= (1LL << 31))
+        return MHA_ERR_UNSUPPORTED;
+    mha::FusedArgs a{B, L, d_model, h, mask_flags, x, w_q, w_k, w_v, kv_lens, o};
+    return launch_status(mha::launch_self_attention_fused_bf16(a, stream));
+}
+
 }  // extern "C"

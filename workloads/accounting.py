@@ -74,4 +74,12 @@ def workload_work(w: Workload, kv_lens=None) -> dict:
         out["out_proj"] = {"flops": gemm_flops(M, w.d_model, n),
                            "bytes": gemm_bytes(M, w.d_model, n, w.dtype)}
     out["total_flops"] = sum(v["flops"] for v in out.values() if isinstance(v, dict))
+    if w.block:
+        # The projections and the attention as one kernel: X and the weights
+        # read once, O written once, Q/K/V never leave the chip.
+        e = ELEM_BYTES[w.dtype]
+        out["self_attention_fused"] = {
+            "flops": out["project_qkv"]["flops"] + att_f,
+            "bytes": e * (M * w.d_model + 3 * w.d_model * n + M * n)
+                     + (4 * w.B if w.mask & 1 else 0)}
     return out
