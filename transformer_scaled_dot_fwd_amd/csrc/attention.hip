@@ -370,7 +370,7 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
                     bf16x4 out;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[qb][db][4 * rg + e] * inv);
-                    *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * half) = out;
+                    store_stream((bf16x4*)(orow + 32 * db + 8 * rg + 4 * half), out);
                 }
         }
     }
@@ -598,8 +598,8 @@ __global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
         const int r = 8 * i + (lane >> 3), c = lane & 7;
         const int qi = wq0 + r;
         if (qi < Lq)
-            *(bf16x8*)(op + (size_t)qi * rs + 8 * c) =
-                *(const bf16x8*)(stg + r * 128 + 16 * (c ^ (r & 7)));
+            store_stream((bf16x8*)(op + (size_t)qi * rs + 8 * c),
+                         *(const bf16x8*)(stg + r * 128 + 16 * (c ^ (r & 7))));
     }
 }
 

@@ -126,6 +126,14 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Output store that bypasses cache retention (nontemporal): results are
+// written once and never read back by the kernel, and keeping them out of
+// L2 spares the writeback of dirty lines when the kernel ends.
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, T v) {
+    __builtin_nontemporal_store(v, p);
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;
 #pragma unroll

@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
         const int r = 8 * i + (lane >> 3), c = lane & 7;
         const int qi = wq0 + r;
         if (qi < L)
-            *(bf16x8*)(op + (size_t)qi * N + 8 * c) =
-                *(const bf16x8*)(stg + r * 128 + 16 * (c ^ (r & 7)));
+            store_stream((bf16x8*)(op + (size_t)qi * N + 8 * c),
+                         *(const bf16x8*)(stg + r * 128 + 16 * (c ^ (r & 7))));
     }
 }
 

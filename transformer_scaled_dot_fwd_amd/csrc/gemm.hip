@@ -242,7 +242,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, in
         const int r = idx / ROW_CHUNKS, c = idx % ROW_CHUNKS;
         const int m = m0 + r, n = n0 + 8 * c;
         if (m < M && n < N)
-            *(bf16x8*)(Y + (size_t)m * N + n) = *(const bf16x8*)(so + r * OPITCH + c * 16);
+            store_stream((bf16x8*)(Y + (size_t)m * N + n), *(const bf16x8*)(so + r * OPITCH + c * 16));
     }
 }
 
