@@ -592,7 +592,8 @@ __global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
             const int chunk = (4 * db + rg) ^ (l32 & 7);
             *(bf16x4*)(stg + l32 * 128 + 16 * chunk + 8 * half) = out;
         }
-    barrier_lds();
+    // The staged rows are this wave's own, and one wave's LDS accesses take
+    // effect in program order: no barrier before reading them back.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 8 * i + (lane >> 3), c = lane & 7;

@@ -22,16 +22,24 @@ constexpr int FL = 128;                               // rows (tokens) per batch
 constexpr int FKT = 32;                               // keys per attention tile
 constexpr int FBK = 32;                               // k step of the projection
 constexpr int FST = 3;                                // projection ring depth
-constexpr int FX_BYTES = FL * FBK * 2;                // X stage: 128 rows of 64 bytes
-constexpr int FW_MAT = FBK * 64 * 2;                  // one weight slab: 32 rows of 128 bytes
+constexpr int FX_ROW = FBK * 2;                       // bytes of an X stage row
+constexpr int FX_BYTES = FL * FX_ROW;                 // X stage: 128 rows
+constexpr int FW_MAT = FBK * 64 * 2;                  // one weight slab: FBK rows of 128 bytes
 constexpr int FW_BYTES = 3 * FW_MAT;                  // W stage: the head's slabs of W^Q, W^K, W^V
-constexpr int FRING = FST * (FX_BYTES + FW_BYTES);    // 60 KB
+constexpr int FRING = FST * (FX_BYTES + FW_BYTES);
 constexpr int FTILE = FL * 64 * 2;                    // one of Q, K, V in LDS: 16 KB
 constexpr int FSMEM = FRING > 3 * FTILE ? FRING : 3 * FTILE;
-constexpr int F_PER_STAGE = 2 + 3;                    // direct loads per wave per stage
+constexpr int FX_INSTR = FX_BYTES / 1024 / 4;         // 1 KB direct loads per wave: X
+constexpr int FW_INSTR = FW_MAT / 1024 / 4;           //   and each weight slab
+constexpr int F_PER_STAGE = FX_INSTR + 3 * FW_INSTR;  // direct loads per wave per stage
+static_assert((FBK == 32 || FBK == 64) && (FST == 2 || FST == 3), "projection pipeline");
 
-// X stage: row r holds 4 chunks of 16 bytes (k = 8c .. 8c+7) at c ^ ((r >> 1) & 3).
-__device__ __forceinline__ int fx_chunk(int r, int c) { return c ^ ((r >> 1) & 3); }
+// X stage: row r holds FBK/8 chunks of 16 bytes (k = 8c .. 8c+7), chunk c at
+// c ^ ((r >> 1) & 3) for rows of 64 bytes, c ^ (r & 7) for rows of 128
+// bytes, so the 16-byte row reads of consecutive rows spread over the banks.
+__device__ __forceinline__ int fx_chunk(int r, int c) {
+    return FBK == 32 ? c ^ ((r >> 1) & 3) : c ^ (r & 7);
+}
 
 template <bool PAD, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
@@ -58,6 +66,10 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
     const int b = bh / H;
     const int hh = bh - b * H;
     const int N = H * 64;  // row length of each weight matrix
+    // The row's length is read first, so its latency hides under the
+    // projection's loads.
+    int kv_end = L;
+    if (PAD) kv_end = min(max(kv_lens[b], 0), L);
 
     // ---- projection: D^T = W^T X^T, 192 features x 128 tokens ----
     // Wave (wm, wn) owns tokens 64 wm .. +63 (two 32-blocks) and features
@@ -67,18 +79,20 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
         make_rsrc(x + (size_t)b * L * DM, (uint32_t)((size_t)L * DM * 2));
     const bf16* wbase[3] = {wq + hh * 64, wk + hh * 64, wv + hh * 64};
     const uint32_t w_bytes = (uint32_t)(((size_t)(DM - 1) * N + 64) * 2);
-    // Direct loads: X stage = 8 slices of 1 KB (16 rows of 64 bytes), wave
-    // w loads slices w and w + 4; W stage = 3 slabs of 4 KB, wave w loads
-    // rows 8w .. 8w+7 of each.
-    uint32_t xoff[2], woff;
+    // Direct loads in slices of 1 KB: wave w loads slices w, w + 4, ... of
+    // the X stage (1024 / FX_ROW rows each) and of each weight slab (8 rows
+    // of 128 bytes each).
+    constexpr int XC = FX_ROW / 16;  // chunks per X row
+    uint32_t xoff[FX_INSTR], woff[FW_INSTR];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int r = 16 * (wave + 4 * u) + (lane >> 2);
-        xoff[u] = (uint32_t)(r * DM + 8 * fx_chunk(r, lane & 3)) * 2;
+    for (int u = 0; u < FX_INSTR; ++u) {
+        const int r = (1024 / FX_ROW) * (wave + 4 * u) + lane / XC;
+        xoff[u] = (uint32_t)(r * DM + 8 * fx_chunk(r, lane % XC)) * 2;
     }
-    {
-        const int r = 8 * wave + (lane >> 3);
-        woff = (uint32_t)(r * N + 8 * ((lane & 7) ^ v_swz(r))) * 2;
+#pragma unroll
+    for (int u = 0; u < FW_INSTR; ++u) {
+        const int r = 8 * (wave + 4 * u) + (lane >> 3);
+        woff[u] = (uint32_t)(r * N + 8 * ((lane & 7) ^ v_swz(r))) * 2;
     }
     auto sX = [&](int st) { return smem + st * FX_BYTES; };
     auto sW = [&](int st) { return smem + FST * FX_BYTES + st * FW_BYTES; };
@@ -87,10 +101,14 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
         const uint32_t xk = (uint32_t)kt * FBK * 2;
         const uint32_t wk_ = (uint32_t)((size_t)kt * FBK * N * 2);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) load_lds16(xr, xs + (wave + 4 * u) * 1024, xoff[u] + xk);
+        for (int u = 0; u < FX_INSTR; ++u)
+            load_lds16(xr, xs + (wave + 4 * u) * 1024, xoff[u] + xk);
 #pragma unroll
-        for (int u = 0; u < 3; ++u)
-            load_lds16(make_rsrc(wbase[u], w_bytes), ws + u * FW_MAT + wave * 1024, woff + wk_);
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int u = 0; u < FW_INSTR; ++u)
+                load_lds16(make_rsrc(wbase[m], w_bytes), ws + m * FW_MAT + (wave + 4 * u) * 1024,
+                           woff[u] + wk_);
     };
 
     f32x16 acc[3][2];
@@ -122,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const int r = 64 * wm + 32 * mb + l32;
-            bx[mb] = *(const bf16x8*)(xs + r * 64 + (fx_chunk(r, 2 * k16 + half) << 4));
+            bx[mb] = *(const bf16x8*)(xs + r * FX_ROW + (fx_chunk(r, 2 * k16 + half) << 4));
         }
     };
     const int n_k = DM / FBK;
@@ -133,17 +151,18 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
         else wait_vmcnt<0>();
         barrier_lds();  // step kt visible everywhere; the stage of step kt-1 is free
         if (kt + FST - 1 < n_k) issue(kt + FST - 1, (st + FST - 1) % FST);
+        // operands of slice i + 1 are read while the MFMAs of slice i run
         read_ops(st, 0, opA[0], opB[0]);
         __builtin_amdgcn_sched_barrier(0);
-        read_ops(st, 1, opA[1], opB[1]);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k16 = 0; k16 < 2; ++k16) {
+        for (int k16 = 0; k16 < FBK / 16; ++k16) {
+            if (k16 + 1 < FBK / 16) read_ops(st, k16 + 1, opA[(k16 + 1) & 1], opB[(k16 + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 3; ++j)
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
-                    acc[j][mb] = mfma32(opA[k16][j], opB[k16][mb], acc[j][mb]);
+                    acc[j][mb] = mfma32(opA[k16 & 1][j], opB[k16 & 1][mb], acc[j][mb]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -162,8 +181,6 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
     // K and V rows at or past the row's length are stored as zeros: like
     // the rows the attention kernels never load, whatever X holds there
     // cannot reach the output.
-    int kv_end = L;
-    if (PAD) kv_end = min(max(kv_lens[b], 0), L);
     barrier_lds();  // every wave is done with the projection ring
     char* const sQ = smem;
     char* const sK = smem + FTILE;
@@ -175,14 +192,18 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
         char* const dst = mat == 0 ? sQ : (mat == 1 ? sK : sV);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const int m = 64 * wm + 32 * mb + l32;
+            const int m0 = 64 * wm + 32 * mb;  // the block's first token (wave-uniform)
+            const int m = m0 + l32;
             const int swz = mat == 2 ? v_swz(m) : k_swz(m);
+            // Only a K or V block that reaches the length needs the zeroing.
+            const bool clip = mat != 0 && m0 + 32 > kv_end;
+            const bool keep = m < kv_end;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                bf16x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v4[e] = (mat == 0 || m < kv_end) ? (bf16)acc[j][mb][4 * q4 + e] : (bf16)0.0f;
+                const f32x4 f = {acc[j][mb][4 * q4], acc[j][mb][4 * q4 + 1],
+                                 acc[j][mb][4 * q4 + 2], acc[j][mb][4 * q4 + 3]};
+                bf16x4 v4 = __builtin_convertvector(f, bf16x4);
+                if (clip && !keep) v4 = bf16x4{};
                 const int chunk = 4 * (fb & 1) + q4;
                 *(bf16x4*)(dst + m * 128 + ((chunk ^ swz) << 4) + 8 * half) = v4;
             }
@@ -283,11 +304,12 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
     }
 
     // ---- O = acc / l (0 without a legal key), staged over this wave's Q
-    // rows (read above by this wave only) and written as whole rows ----
+    // rows and written as whole rows.  Only this wave reads or writes
+    // those rows, and one wave's LDS accesses take effect in program
+    // order, so the staging needs no barrier. ----
     const float l_tot = sum_halves(l_part);
     const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
     char* stg = sQ + wq0 * 128;
-    barrier_lds();  // every lane of every wave holds its Q operands
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -298,7 +320,6 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
             const int chunk = (4 * db + rg) ^ (l32 & 7);
             *(bf16x4*)(stg + l32 * 128 + 16 * chunk + 8 * half) = out;
         }
-    barrier_lds();
     bf16* op = o + ((size_t)b * L * H + hh) * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
