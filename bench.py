@@ -59,9 +59,11 @@ def log(*a):
 
 
 def source_sha(name: str) -> str:
+    """Hash of a kernel's source file and of every header beside it."""
     h = hashlib.sha256()
-    for p in sorted({KERNEL_SOURCES[name], os.path.join(os.path.dirname(KERNEL_SOURCES[name]),
-                                                       "device.h")}):
+    src = KERNEL_SOURCES[name]
+    d = os.path.dirname(src)
+    for p in [src] + sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".h")):
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 

@@ -116,7 +116,8 @@ int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v,
  *   outputs must not overlap the inputs or each other.
  *
  * Supported: MHA_BF16 and MHA_F32; d_model % 64 == 0, h*d_k % 64 == 0,
- * d_k == d_v.
+ * d_k == d_v; for MHA_BF16 also d_model * h*d_k < 2^30 and d_model < 2^23
+ * (32-bit byte offsets within a weight matrix and 128 rows of X).
  */
 int mha_project_qkv(mha_dtype dt, int B, int Lq, int Lk, int d_model, int h,
                     int d_k, int d_v,
@@ -132,7 +133,9 @@ int mha_project_qkv(mha_dtype dt, int B, int Lq, int Lk, int d_model, int h,
  *   w_o  [h*d_v, d_model]
  *   y    [B, Lq, d_model]                  output; must not overlap o, w_o
  *
- * Supported: MHA_BF16 and MHA_F32; d_model % 64 == 0, h*d_v % 64 == 0.
+ * Supported: MHA_BF16 and MHA_F32; d_model % 64 == 0, h*d_v % 64 == 0; for
+ * MHA_BF16 also h*d_v * d_model < 2^30 and h*d_v < 2^23 (32-bit byte offsets
+ * within W^O and 128 rows of o).
  */
 int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
                  const void* o, const void* w_o, void* y, hipStream_t stream);

@@ -129,3 +129,13 @@ def test_python_binding_checks_before_calling():
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):          # host tensors are refused
         mha.mha_forward(q, q, q)
+
+
+def test_projection_size_limits(L):
+    """bf16 GEMMs address a weight matrix with 32-bit byte offsets: weights of
+    2^30 elements or more are refused (nothing is launched)."""
+    P = L.mha_project_qkv
+    # (dt, B, Lq, Lk, d_model, h, d_k, d_v, x_q, x_kv, w_q, w_k, w_v, q, k, v, stream)
+    assert P(BF16, 1, 8, 8, 32768, 512, 64, 64, *([FAKE] * 8), None) == UNSUPPORTED
+    O = L.mha_out_proj
+    assert O(BF16, 1, 8, 512, 64, 32768, FAKE, FAKE, FAKE, None) == UNSUPPORTED

@@ -108,7 +108,10 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmBatch& batch, int N, in
     // of W read as zeros; columns past N only feed outputs that are not
     // stored).
     const bf16* X = (const bf16*)P.x + (size_t)m0 * K;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)((size_t)(M - m0) * K * 2));
+    // (Only the tile's own rows are in range, so the byte range stays below
+    // 2^32 whatever M is.)
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(X, (uint32_t)((size_t)min(M - m0, BM) * K * 2));
     const bf16* W = (const bf16*)P.w + n0;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)(((size_t)K * N - n0) * 2));
 

@@ -76,6 +76,11 @@ int mha_project_qkv(mha_dtype dt, int B, int Lq, int Lk, int d_model, int h, int
     if (d_k != d_v) return MHA_ERR_UNSUPPORTED;
     const long long N = (long long)h * d_k;
     if (d_model % 64 != 0 || N % 64 != 0 || N > INT_MAX) return MHA_ERR_UNSUPPORTED;
+    // bf16: a weight matrix and 128 rows of X are addressed with 32-bit byte
+    // offsets.
+    if (dt == MHA_BF16 &&
+        ((long long)d_model * N * 2 >= (1LL << 31) || (long long)d_model * 256 >= (1LL << 31)))
+        return MHA_ERR_UNSUPPORTED;
     if (Mq > INT_MAX || Mkv > INT_MAX) return MHA_ERR_UNSUPPORTED;
 
     mha::GemmProblem probs[3];
@@ -101,6 +106,9 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model, const
     if (!aligned16(o) || !aligned16(w_o) || !aligned16(y)) return MHA_ERR_INVALID_ARG;
     const long long K = (long long)h * d_v;
     if (d_model % 64 != 0 || K % 64 != 0 || K > INT_MAX || M > INT_MAX)
+        return MHA_ERR_UNSUPPORTED;
+    // bf16: W^O and 128 rows of O are addressed with 32-bit byte offsets.
+    if (dt == MHA_BF16 && (K * d_model * 2 >= (1LL << 31) || K * 256 >= (1LL << 31)))
         return MHA_ERR_UNSUPPORTED;
     mha::GemmProblem prob{o, w_o, y, (int)M};
     const hipError_t e = (dt == MHA_BF16)
