@@ -220,14 +220,16 @@ def traffic_for(name, launches_key):
     return e.get("bytes_per_launch")
 
 
-def attention_sweep(dev, steps, warmup):
+def attention_sweep(dev, steps, warmup, workloads=None):
     """Attention alone at the base (h=8) and big (h=16) shapes, L >= 1024,
-    plus the long causal workload."""
+    plus the long causal workload (or the given workloads)."""
     import torch
     import transformer_scaled_dot_fwd_amd as mha
     from workloads import accounting, configs
     out = []
-    for w in [configs.get("c5")] + configs.sweep():
+    if workloads is None:
+        workloads = [configs.get("c5")] + configs.sweep()
+    for w in workloads:
         inp = configs.make_inputs(w)
         one = working_set_bytes([inp["q"], inp["k"], inp["v"], inp["q"]])
         n_sets = max(2, min(16, math.ceil(ROTATE_BYTES / one)))
@@ -241,7 +243,7 @@ def attention_sweep(dev, steps, warmup):
         sec = kernel_time(fn, sets, max(steps // 4, 2 * n_sets), warmup)
         flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, inp["kv_lens"])
         tf = flops / sec / 1e12
-        out.append({"workload": w.name, "B": w.B, "h": w.h, "L": w.Lq,
+        out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L": w.Lq,
                     "mask": "causal" if w.mask & 2 else "none", "us": round(sec * 1e6, 2),
                     "tflops": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)})
         log(f"  sweep {w.name}: {sec * 1e6:.1f} us, {tf:.1f} TFLOP/s "
@@ -390,6 +392,8 @@ def main():
                          "gbps": round(b / sec / 1e9, 1), "in_step": name in step_kernels}
 
     sweep = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup)
+    heads = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup,
+                                                       configs.head_sizes())
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inputs, args.cpu_seconds)
@@ -419,6 +423,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "attention_sweep": sweep,
+        "head_size_sweep": heads,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

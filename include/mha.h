@@ -90,7 +90,8 @@ enum {
  * Supported: B, Lq, Lk >= 0 and h >= 1 (B == 0 or Lq == 0 is a no-op;
  * Lk == 0 gives O = 0), d_k == d_v, B*h*ceil(Lq/64) < 2^31, and one batch
  * row of Q or of K/V under 2 GiB (L*h*d_k*elem_size < 2^31);
- * MHA_BF16 with d_k = 64; MHA_F32 with d_k in {8, 16, 32, 64}.
+ * MHA_BF16 with d_k in {16, 32, 64, 128} (the head sizes of [Deep] section
+ * 08, Table 3, rows (A), besides 512); MHA_F32 with d_k in {8, 16, 32, 64}.
  */
 int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v,
                 const void* q, const void* k, const void* v,

@@ -66,7 +66,8 @@ def fwd(L, dt=BF16, B=2, h=2, Lq=8, Lk=8, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, 
     (dict(k=None), INVALID),
     (dict(q=FAKE + 8), INVALID),                  # misaligned
     (dict(dk=64, dv=32), UNSUPPORTED),
-    (dict(dk=32, dv=32), UNSUPPORTED),            # bf16 is built for d = 64
+    (dict(dk=48, dv=48), UNSUPPORTED),            # bf16 is built for d in {16, 32, 64, 128}
+    (dict(dk=256, dv=256), UNSUPPORTED),
     (dict(dt=F32, dk=24, dv=24), UNSUPPORTED),
     (dict(B=0), OK),                              # empty: nothing launched
     (dict(Lq=0, Lk=0, mask=2), OK),

@@ -18,7 +18,9 @@
 namespace mha {
 
 // ---------------------------------------------------------------------------
-// bf16, d = 64: MFMA path.
+// bf16 MFMA path, head size D in {16, 32, 64, 128} (the base shape's 64 and
+// the other head shapes of "Paper Deep Reading", section 08, Table 3, rows
+// (A)).
 //
 // Workgroup = NW waves = one (batch row, head, tile of 32*QB*NW queries).
 // Wave w owns QB blocks of 32 consecutive queries, one query per lane
@@ -29,7 +31,11 @@ namespace mha {
 //                      reads), B = Q (registers, loaded once)
 //   O^T += V^T P^T     A = V^T (LDS transpose reads), B = P (registers)
 //
-// Each A operand (a K or V^T fragment) feeds the wave's QB query blocks.
+// S^T takes D/16 MFMAs per 32 x 32 block and O^T += V^T P^T one MFMA per
+// 16-key chunk and 32-wide d block; for D = 16 the d block is half used (its
+// other 16 rows read whatever the LDS row padding holds and are never
+// stored).  Each A operand (a K or V^T fragment) feeds the wave's QB query
+// blocks.
 // Keeping the query in the lane column makes every per-query quantity (row
 // max, row sum, rescale factor) lane-local, with one exchange between the
 // two half-waves.  The PV contraction runs over keys in the order the S^T
@@ -37,8 +43,8 @@ namespace mha {
 // same order.
 //
 // Software pipeline per wave: the score MFMAs of tile j+1 and the PV MFMAs
-// of tile j are interleaved, one MFMA per two exponentials, with the
-// softmax VALU work of tile j.  Global loads run two tiles ahead.
+// of tile j are interleaved with the softmax VALU work of tile j (for D =
+// 64, one MFMA per two exponentials).  Global loads run two tiles ahead.
 // ---------------------------------------------------------------------------
 #ifndef ATTN_QB1_OCC
 #define ATTN_QB1_OCC 3
@@ -52,19 +58,33 @@ namespace {
 constexpr int D64 = 64;
 constexpr int KT = 32;             // keys per tile
 constexpr int STAGES = 3;          // LDS ring depth
-constexpr int PITCH = D64 + 8;     // LDS row pitch in elements (144 B)
-constexpr int TILE = KT * PITCH;   // elements per K (or V) tile in LDS
 
-template <int NW, int QB, bool PAD, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_bf16_d64(
+// Waves per SIMD the long-row kernel is built for.
+template <int D, int QB>
+constexpr int attn_occupancy() {
+    return D > 64 ? 2 : (QB == 1 ? ATTN_QB1_OCC : 2);
+}
+
+template <int D, int NW, int QB, bool PAD, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
     int n_qtiles, float scale_log2e) {
+    static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head size");
+    constexpr int NKK = D / 16;              // 16-wide k slices of q.k
+    constexpr int DP = D < 32 ? 32 : D;      // d extent the PV blocks cover
+    constexpr int NDB = DP / 32;             // 32-wide d blocks of O
+    constexpr int PITCH = DP + 8;            // LDS row pitch in elements
+    constexpr int TILE = KT * PITCH;         // elements per K (or V) tile in LDS
     constexpr int WQ = 32 * QB;     // queries per wave
     constexpr int BM = WQ * NW;     // queries per workgroup
     constexpr int THREADS = 64 * NW;
-    constexpr int CHUNKS = KT * D64 / 8 / THREADS;  // 16-byte chunks of K (and of V) per thread
-    static_assert(CHUNKS >= 1 && KT * D64 / 8 == CHUNKS * THREADS, "tile load split");
+    constexpr int ROW_CHUNKS = D / 8;                  // 16-byte chunks per K (or V) row
+    constexpr int TILE_CHUNKS = KT * ROW_CHUNKS;       // per K (or V) tile
+    // 16-byte chunks of K (and of V) per thread and tile; for small D only
+    // the first TILE_CHUNKS threads load.
+    constexpr int CHUNKS = TILE_CHUNKS >= THREADS ? TILE_CHUNKS / THREADS : 1;
+    static_assert(TILE_CHUNKS < THREADS || TILE_CHUNKS == CHUNKS * THREADS, "tile load split");
     __shared__ __attribute__((aligned(16))) bf16 sK[STAGES * TILE];
     __shared__ __attribute__((aligned(16))) bf16 sV[STAGES * TILE];
 
@@ -116,31 +136,31 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
     int n_mine = (wq0 < Lq) ? n_tiles : 0;
     if (CAUSAL) n_mine = min(n_mine, (wq0 + WQ + KT - 1) / KT);
 
-    const size_t rs = (size_t)H * D64;  // elements between consecutive positions
-    const bf16* qp = q + ((size_t)b * Lq * H + hh) * D64;
-    const bf16* kp = k + ((size_t)b * Lk * H + hh) * D64;
-    const bf16* vp = v + ((size_t)b * Lk * H + hh) * D64;
-    bf16* op = o + ((size_t)b * Lq * H + hh) * D64;
+    const size_t rs = (size_t)H * D;  // elements between consecutive positions
+    const bf16* qp = q + ((size_t)b * Lq * H + hh) * D;
+    const bf16* kp = k + ((size_t)b * Lk * H + hh) * D;
+    const bf16* vp = v + ((size_t)b * Lk * H + hh) * D;
+    bf16* op = o + ((size_t)b * Lq * H + hh) * D;
 
     // Q as the B operand of S^T = K Q^T: block qb, lane holds query
     // wq0 + 32qb + l32, d = 16kk + 8half .. +7.  Rows past Lq read as zeros.
     const __amdgpu_buffer_rsrc_t qrsrc =
-        make_rsrc(qp, (uint32_t)(((size_t)(Lq - 1) * rs + D64) * sizeof(bf16)));
-    bf16x8 qop[QB][4];
+        make_rsrc(qp, (uint32_t)(((size_t)(Lq - 1) * rs + D) * sizeof(bf16)));
+    bf16x8 qop[QB][NKK];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qi = wq0 + 32 * qb + l32;
         const uint32_t qoff =
             qi < Lq ? (uint32_t)(((size_t)qi * rs + 8 * half) * sizeof(bf16)) : OOB_OFFSET;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
+        for (int kk = 0; kk < NKK; ++kk) qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
     }
 
-    f32x16 acc[QB][2];  // [query block][d block]
+    f32x16 acc[QB][NDB];  // [query block][d block]
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
     float m_run[QB], l_part[QB];  // running max of the raw logits q.k; this lane's row-sum share
@@ -150,18 +170,20 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
         l_part[qb] = 0.0f;
     }
 
-    // Cooperative tile load: KT rows x 128 B of K and of V, 16 B per chunk,
-    // through buffer resources that end at the last legal key row: rows at
-    // or past kv_end read as zeros and are never fetched from memory.
+    // Cooperative tile load: KT rows x 2D bytes of K and of V, 16 B per
+    // chunk, through buffer resources that end at the last legal key row:
+    // rows at or past kv_end read as zeros and are never fetched from memory.
     const uint32_t kv_bytes =
-        kv_end > 0 ? (uint32_t)(((size_t)(kv_end - 1) * rs + D64) * sizeof(bf16)) : 0u;
+        kv_end > 0 ? (uint32_t)(((size_t)(kv_end - 1) * rs + D) * sizeof(bf16)) : 0u;
     const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kp, kv_bytes);
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vp, kv_bytes);
+    const bool loader = TILE_CHUNKS >= THREADS || tid < TILE_CHUNKS;
     uint32_t voff[CHUNKS];  // this thread's chunk offsets inside a tile (loop invariant)
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
         const int c = tid + THREADS * u;
-        voff[u] = (uint32_t)(((size_t)(c >> 3) * rs + (c & 7) * 8) * sizeof(bf16));
+        voff[u] = (uint32_t)(((size_t)(c / ROW_CHUNKS) * rs + (c % ROW_CHUNKS) * 8) *
+                             sizeof(bf16));
     }
     const uint32_t tile_bytes = (uint32_t)((size_t)KT * rs * sizeof(bf16));
     // Two register sets: loads run two tiles ahead of the LDS ring.
@@ -169,7 +191,7 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
     // Unconditional (branch-free) tile load; tiles at or past n_tiles read
     // zeros without touching memory.
     auto gload = [&](int set, int t) {
-        const uint32_t base = t < n_tiles ? (uint32_t)t * tile_bytes : OOB_OFFSET;
+        const uint32_t base = t < n_tiles && loader ? (uint32_t)t * tile_bytes : OOB_OFFSET;
 #pragma unroll
         for (int u = 0; u < CHUNKS; ++u) {
             kreg[set][u] = buffer_load16(krsrc, base + voff[u]);
@@ -177,10 +199,11 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
         }
     };
     auto sstore = [&](int set, int stage) {
+        if (!loader) return;
 #pragma unroll
         for (int u = 0; u < CHUNKS; ++u) {
             const int c = tid + THREADS * u;
-            const int off = stage * TILE + (c >> 3) * PITCH + (c & 7) * 8;
+            const int off = stage * TILE + (c / ROW_CHUNKS) * PITCH + (c % ROW_CHUNKS) * 8;
             *(bf16x8*)(sK + off) = kreg[set][u];
             *(bf16x8*)(sV + off) = vreg[set][u];
         }
@@ -191,7 +214,7 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
     auto scores = [&](int stage, f32x16 (&S)[QB]) {
         const bf16* kt = sK + stage * TILE + l32 * PITCH + 8 * half;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < NKK; ++kk) {
             const bf16x8 a = *(const bf16x8*)(kt + 16 * kk);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
@@ -236,7 +259,7 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
                 const float alpha =
                     grow ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * scale_log2e) : 1.0f;
 #pragma unroll
-                for (int db = 0; db < 2; ++db)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
                 l_part[qb] *= alpha;
@@ -261,13 +284,14 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
         l_part[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part[qb], false);
     };
 
-    // One tile of the pipeline.  Slot s (0 .. 8*QB-1) issues one MFMA and
-    // exponentiates pair s (query block s/8, values 2(s%8), 2(s%8)+1).  The
-    // first 4*QB MFMAs are the scores of tile j+1; the rest are P_j V_j in
-    // (query block, chunk, d block) order, each issued once its P chunk is
-    // complete (chunk (qb, c) is done after pair 8qb + 4c + 3); those not
-    // ready by the last slot run after it.  sched_barrier fences keep the
-    // order.
+    // One tile of the pipeline.  Slot s (0 .. 8*QB-1) exponentiates pair s
+    // (query block s/8, values 2(s%8), 2(s%8)+1) and issues MFMAs
+    // s*NM/NSLOT .. (s+1)*NM/NSLOT - 1 of the tile's NM (one per slot for D =
+    // 64).  The first NKK*QB MFMAs are the scores of tile j+1; the rest are
+    // P_j V_j in (query block, chunk, d block) order, each issued once its P
+    // chunk is complete (chunk (qb, c) is done after pair 8qb + 4c + 3);
+    // those not ready at their slot run after the last slot.  sched_barrier
+    // fences keep the order.
     auto tile_step = [&](int j, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
         // LDS operands, issued up front: K of tile j+1, V^T of tile j.  P
         // chunk c covers keys 16c + {0..3, 8..11} (k = 0..7, lanes < 32) and
@@ -275,16 +299,16 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
         // operand: lane group g reads columns 32db + 16(g&1) + j of rows
         // base + 0..3 and base + 8..11, base = 16c + 4(g>>1).
         const bf16* kt = sK + ((j + 1) % STAGES) * TILE + l32 * PITCH + 8 * half;
-        bf16x8 ka[4];
+        bf16x8 ka[NKK];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[kk] = *(const bf16x8*)(kt + 16 * kk);
+        for (int kk = 0; kk < NKK; ++kk) ka[kk] = *(const bf16x8*)(kt + 16 * kk);
         const bf16* vt = sV + (j % STAGES) * TILE;
-        bf16x8 va[2][2];  // [chunk][d block]
+        bf16x8 va[2][NDB];  // [chunk][d block]
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int row = 16 * c + 4 * (g >> 1) + (i16 >> 2);
 #pragma unroll
-            for (int db = 0; db < 2; ++db) {
+            for (int db = 0; db < NDB; ++db) {
                 const int col = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
                 va[c][db] = join(lds_read_tr(vt + row * PITCH + col),
                                  lds_read_tr(vt + (row + 8) * PITCH + col));
@@ -303,26 +327,40 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
         // arbiter favours a wave in its MFMA phase over one in its softmax
         // or load phase.
         __builtin_amdgcn_s_setprio(1);
-        constexpr int NS = 4 * QB;  // score MFMAs
+        constexpr int NS = NKK * QB;           // score MFMAs
+        constexpr int NPV = 2 * NDB * QB;      // PV MFMAs
+        constexpr int NM = NS + NPV;
         constexpr int NSLOT = 8 * QB;
+        // PV MFMA n (0 .. NPV-1): query block, chunk, d block; ready at slot
+        // 8qb + 4c + 4.
+        auto pv_ready = [&](int n, int s) {
+            const int qb = n / (2 * NDB), c = (n / NDB) % 2;
+            return s >= 8 * qb + 4 * c + 4;
+        };
+        auto pv = [&](int n) {
+            const int qb = n / (2 * NDB), c = (n / NDB) % 2, db = n % NDB;
+            acc[qb][db] = mfma32(va[c][db], pop[qb][c], acc[qb][db]);
+        };
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s) {
             __builtin_amdgcn_sched_barrier(0);
-            if (s < NS) {
-                const int qb = s % QB, kk = s / QB;
-                Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
-            } else {
-                const int n = s - NS, qb = n / 4, c = (n / 2) % 2, db = n % 2;
-                if (s >= 8 * qb + 4 * c + 4) acc[qb][db] = mfma32(va[c][db], pop[qb][c], acc[qb][db]);
+#pragma unroll
+            for (int m = s * NM / NSLOT; m < (s + 1) * NM / NSLOT; ++m) {
+                if (m < NS) {
+                    const int qb = m % QB, kk = m / QB;
+                    Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
+                } else if (pv_ready(m - NS, s)) {
+                    pv(m - NS);
+                }
             }
             exp_pair(Scur, mc, pop, s / 8, s % 8);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int n = 0; n < 4 * QB; ++n) {
-            const int s = NS + n, qb = n / 4, c = (n / 2) % 2, db = n % 2;
-            if (!(s >= 8 * qb + 4 * c + 4)) acc[qb][db] = mfma32(va[c][db], pop[qb][c], acc[qb][db]);
-        }
+        for (int s = 0; s < NSLOT; ++s)
+#pragma unroll
+            for (int m = s * NM / NSLOT; m < (s + 1) * NM / NSLOT; ++m)
+                if (m >= NS && !pv_ready(m - NS, s)) pv(m - NS);
         __builtin_amdgcn_s_setprio(0);
     };
 
@@ -364,13 +402,16 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? ATTN_QB1_OCC : 2) void attn_fwd_
         if (qi < Lq) {
             bf16* orow = op + (size_t)qi * rs;
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    bf16x4 out;
+                    const int col = 32 * db + 8 * rg + 4 * half;
+                    if (D >= 32 || col < D) {
+                        bf16x4 out;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[qb][db][4 * rg + e] * inv);
-                    store_stream((bf16x4*)(orow + 32 * db + 8 * rg + 4 * half), out);
+                        for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[qb][db][4 * rg + e] * inv);
+                        store_stream((bf16x4*)(orow + col), out);
+                    }
                 }
         }
     }
@@ -717,7 +758,7 @@ hipError_t launch_f32_d(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int NW, int QB>
+template <int D, int NW, int QB>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
     constexpr int BM = 32 * QB * NW;
     const int n_qtiles = (a.Lq + BM - 1) / BM;
@@ -730,19 +771,19 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
     bf16* o = (bf16*)a.o;
     switch (a.mask) {
         case 0:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, QB, false, false>), grid, block, 0, stream,
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, false, false>), grid, block, 0, stream,
                                q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         case 1:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, QB, true, false>), grid, block, 0, stream,
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, true, false>), grid, block, 0, stream,
                                q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         case 2:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, QB, false, true>), grid, block, 0, stream,
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, false, true>), grid, block, 0, stream,
                                q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
         default:
-            hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, QB, true, true>), grid, block, 0, stream,
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, true, true>), grid, block, 0, stream,
                                q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
             break;
     }
@@ -788,11 +829,19 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     // triangle.  Longer rows run 64 queries per wave, halving the LDS reads
     // per MFMA.
     // Rows of at most 128 (256) keys: the whole K/V row in LDS at once.
+    // Head sizes other than 64 run the long-row kernel at every length, 32
+    // queries per wave.
+    switch (a.D) {
+        case 16: return launch_bf16<16, ATTN_NW, 1>(a, stream);
+        case 32: return launch_bf16<32, ATTN_NW, 1>(a, stream);
+        case 128: return launch_bf16<128, 8, 1>(a, stream);
+        default: break;
+    }
     if (a.Lk <= 128) return launch_short_bf16<4>(a, stream);
     if (a.Lk <= 256) return launch_short_bf16<8>(a, stream);
     const bool causal = (a.mask & 2) != 0;  // AttnArgs::mask bit 1
-    if (a.Lq <= 512 || (causal && a.Lq <= 2048)) return launch_bf16<ATTN_NW, 1>(a, stream);
-    return launch_bf16<ATTN_NW, 2>(a, stream);
+    if (a.Lq <= 512 || (causal && a.Lq <= 2048)) return launch_bf16<64, ATTN_NW, 1>(a, stream);
+    return launch_bf16<64, ATTN_NW, 2>(a, stream);
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {

@@ -53,7 +53,7 @@ int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v, co
 
     mha::AttnArgs a{B, h, Lq, Lk, d_k, mask_flags, q, k, v, kv_lens, o};
     if (dt == MHA_BF16) {
-        if (d_k != 64) return MHA_ERR_UNSUPPORTED;
+        if (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128) return MHA_ERR_UNSUPPORTED;
         return launch_status(mha::launch_attention_bf16(a, stream));
     }
     if (d_k != 8 && d_k != 16 && d_k != 32 && d_k != 64) return MHA_ERR_UNSUPPORTED;

@@ -91,11 +91,27 @@ def sweep():
     return out
 
 
+def head_sizes():
+    """The other head shapes of the base model's width (d_model 512; Deep-
+    reading page section 08, Table 3, rows (A)): h=32 d=16, h=16 d=32, h=4
+    d=128, at L in {1024, 4096} with B = 24576 / L, no mask and causal."""
+    out = []
+    n = 80
+    for h, d in ((32, 16), (16, 32), (4, 128)):
+        for L in (1024, 4096):
+            for mask, tag in ((MASK_NONE, "nomask"), (MASK_CAUSAL, "causal")):
+                n += 1
+                out.append(Workload(f"heads_h{h}_d{d}_L{L}_{tag}", n, B=24576 // L, h=h,
+                                    Lq=L, Lk=L, d=d, dtype="bf16", mask=mask,
+                                    description=f"h={h} d={d} L={L} B={24576 // L} bf16 {tag}"))
+    return out
+
+
 def get(name: str) -> Workload:
     name = ALIASES.get(name, name)
     if name in CONFIGS:
         return CONFIGS[name]
-    for w in sweep():
+    for w in sweep() + head_sizes():
         if w.name == name:
             return w
     raise KeyError(name)
