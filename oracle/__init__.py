@@ -11,7 +11,9 @@ marshals numpy arrays.  What each function computes, and the passages of the
 pages it follows, is written in ``oracle.c``:
 
 * ``attention``      -- softmax(Q K^T / sqrt(d_k) + M) V for every (b, head);
-  Deep-reading page section 04, attention equation with the mask M.
+  Deep-reading page section 04, attention equation with the mask M; with
+  ``window=w``, restricted self-attention (keys within w positions of the
+  query; Deep-reading page section 05, complexity table).
 * ``attention_rows`` -- the same definition for a sampled list of rows.
 * ``matmul``         -- Y = A W (the projections and W^O of MultiHead;
   slide "Multi-Head Attention").
@@ -86,10 +88,11 @@ class Oracle:
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
         L, P = ctypes.c_long, ctypes.c_void_p
-        lib.oracle_attention.argtypes = [L, L, L, L, L, L, P, P, P, ctypes.c_int, P, P, P, P]
+        lib.oracle_attention.argtypes = [L, L, L, L, L, L, P, P, P, ctypes.c_int, P, L, P, P,
+                                         P]
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = [L, L, L, L, L, L, P, P, P, ctypes.c_int, P,
-                                              L, P, P]
+                                              L, L, P, P]
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_matmul.argtypes = [L, L, L, P, P, P]
         lib.oracle_matmul.restype = ctypes.c_int
@@ -107,12 +110,13 @@ class Oracle:
         self.lib.oracle_set_num_threads(int(n))
 
     def attention(self, q, k, v, mask: int = MASK_NONE, kv_lens=None,
-                  return_p: bool = False, return_s: bool = False):
+                  return_p: bool = False, return_s: bool = False, window=None):
         """O = softmax(Q K^T / sqrt(d_k) + M) V in fp64.
 
         q [B, Lq, h, d_k], k [B, Lk, h, d_k], v [B, Lk, h, d_v] (BLHD);
         returns o [B, Lq, h, d_v] and, on request, P and the scaled logits S,
-        both [B, h, Lq, Lk] (S is -inf where masked).
+        both [B, h, Lq, Lk] (S is -inf where masked).  window: half-width w
+        of restricted self-attention (keys with |i - j| <= w), or None.
         """
         q, k, v = _f64(q), _f64(k), _f64(v)
         B, Lq, h, dk = q.shape
@@ -125,7 +129,8 @@ class Oracle:
         p = np.zeros((B, h, Lq, Lk), dtype=np.float64) if return_p else None
         s = np.zeros((B, h, Lq, Lk), dtype=np.float64) if return_s else None
         rc = self.lib.oracle_attention(B, h, Lq, Lk, dk, dv, _ptr(q), _ptr(k), _ptr(v),
-                                       int(mask), _ptr(lens), _ptr(o), _ptr(p), _ptr(s))
+                                       int(mask), _ptr(lens), -1 if window is None else int(window),
+                                       _ptr(o), _ptr(p), _ptr(s))
         if rc != 0:
             raise ValueError("oracle_attention rejected its arguments")
         if return_p or return_s:
@@ -137,7 +142,7 @@ class Oracle:
             return out
         return o
 
-    def attention_rows(self, q, k, v, rows, mask: int = MASK_NONE, kv_lens=None):
+    def attention_rows(self, q, k, v, rows, mask: int = MASK_NONE, kv_lens=None, window=None):
         """The attention definition for selected rows only.
 
         rows: int array [n, 3] of (b, head, i).  Returns [n, d_v] fp64, row n
@@ -151,8 +156,9 @@ class Oracle:
         lens = _lens(kv_lens, B) if (mask & MASK_KEY_PADDING) else None
         o = np.zeros((rows.shape[0], dv), dtype=np.float64)
         rc = self.lib.oracle_attention_rows(B, h, Lq, Lk, dk, dv, _ptr(q), _ptr(k),
-                                            _ptr(v), int(mask), _ptr(lens), rows.shape[0],
-                                            _ptr(rows), _ptr(o))
+                                            _ptr(v), int(mask), _ptr(lens),
+                                            -1 if window is None else int(window),
+                                            rows.shape[0], _ptr(rows), _ptr(o))
         if rc != 0:
             raise ValueError("oracle_attention_rows rejected its arguments")
         return o

@@ -35,6 +35,13 @@
  * Readings taken where the pages are silent (each is listed with its reason
  * in the design notes):
  *   - causal: key j is legal for query i iff j <= i (the diagonal is kept);
+ *   - restricted (windowed) self-attention with half-width w: key j is legal
+ *     for query i iff |i - j| <= w, a neighbourhood of r = 2w + 1 positions
+ *     centred on the query, so a layer costs O(r n d) and a signal crosses n
+ *     positions in O(n / r) layers ([Deep] section 05, the complexity table,
+ *     "Restricted self-attention"; [Slides] slide "Limitations and Future
+ *     Work").  It combines with the other masks as their union, and needs
+ *     Lq == Lk (query and key positions on one axis);
  *   - key padding: key j is legal iff j < len_b, with len_b clamped to
  *     [0, Lk];
  *   - a query row with no legal key outputs 0 (softmax of all -inf is 0/0);
@@ -84,11 +91,13 @@ void oracle_set_num_threads(int n)
 }
 
 /* Is key j legal for query i of batch row b?  [Deep] section 03 "Decoder
- * layer" (future connections are illegal) and section 04 (padding). */
-static int key_is_legal(int mask_flags, long len_b, long i, long j)
+ * layer" (future connections are illegal), section 04 (padding), section 05
+ * (restricted self-attention: window >= 0 is the half-width, -1 none). */
+static int key_is_legal(int mask_flags, long len_b, long window, long i, long j)
 {
     if ((mask_flags & ORACLE_MASK_KEY_PADDING) && j >= len_b) return 0;
     if ((mask_flags & ORACLE_MASK_CAUSAL) && j > i) return 0;
+    if (window >= 0 && (j < i - window || j > i + window)) return 0;
     return 1;
 }
 
@@ -109,7 +118,7 @@ static long clamped_len(int mask_flags, const int32_t* kv_lens, long b, long Lk)
  */
 static void attention_row(long B, long h, long Lq, long Lk, long d_k, long d_v,
                           const double* q, const double* k, const double* v,
-                          int mask_flags, const int32_t* kv_lens,
+                          int mask_flags, const int32_t* kv_lens, long window,
                           long b, long t, long i,
                           double* o_row, double* p_row, double* s_row,
                           double* logits, double* weights)
@@ -122,7 +131,7 @@ static void attention_row(long B, long h, long Lq, long Lk, long d_k, long d_v,
     /* MatMul, then Scale, then Mask ([Deep] section 04, Figure 2 left). */
     int any_legal = 0;
     for (long j = 0; j < Lk; ++j) {
-        if (!key_is_legal(mask_flags, len_b, i, j)) {
+        if (!key_is_legal(mask_flags, len_b, window, i, j)) {
             logits[j] = -INFINITY;
             continue;
         }
@@ -161,7 +170,7 @@ static void attention_row(long B, long h, long Lq, long Lk, long d_k, long d_v,
      * and their V rows are not read. */
     for (long e = 0; e < d_v; ++e) o_row[e] = 0.0;
     for (long j = 0; j < Lk; ++j) {
-        if (!key_is_legal(mask_flags, len_b, i, j)) continue;
+        if (!key_is_legal(mask_flags, len_b, window, i, j)) continue;
         const double* vj = v + ((b * Lk + j) * h + t) * d_v;
         for (long e = 0; e < d_v; ++e) o_row[e] += weights[j] * vj[e];
     }
@@ -170,16 +179,18 @@ static void attention_row(long B, long h, long Lq, long Lk, long d_k, long d_v,
 /*
  * O = softmax(Q K^T / sqrt(d_k) + M) V for every (b, t).
  * kv_lens: [B] int32, read only when KEY_PADDING is set (may be NULL
- * otherwise).  p and s may be NULL.  Returns 0, or -1 on bad arguments.
+ * otherwise).  window: the restricted-attention half-width, or -1 for none.
+ * p and s may be NULL.  Returns 0, or -1 on bad arguments.
  */
 int oracle_attention(long B, long h, long Lq, long Lk, long d_k, long d_v,
                      const double* q, const double* k, const double* v,
-                     int mask_flags, const int32_t* kv_lens,
+                     int mask_flags, const int32_t* kv_lens, long window,
                      double* o, double* p, double* s)
 {
-    if (B < 0 || h < 1 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1) return -1;
+    if (B < 0 || h < 1 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1 || window < -1) return -1;
     if ((mask_flags & ORACLE_MASK_KEY_PADDING) && !kv_lens && B > 0) return -1;
     if ((mask_flags & ORACLE_MASK_CAUSAL) && Lq != Lk) return -1;
+    if (window >= 0 && Lq != Lk) return -1;
     const long rows = B * h * Lq;
     int failed = 0;
 #pragma omp parallel
@@ -198,7 +209,7 @@ int oracle_attention(long B, long h, long Lq, long Lk, long d_k, long d_v,
                 double* o_row = o + ((b * Lq + i) * h + t) * d_v;
                 double* p_row = p ? p + ((b * h + t) * Lq + i) * Lk : NULL;
                 double* s_row = s ? s + ((b * h + t) * Lq + i) * Lk : NULL;
-                attention_row(B, h, Lq, Lk, d_k, d_v, q, k, v, mask_flags, kv_lens,
+                attention_row(B, h, Lq, Lk, d_k, d_v, q, k, v, mask_flags, kv_lens, window,
                               b, t, i, o_row, p_row, s_row, logits, weights);
             }
         }
@@ -215,12 +226,14 @@ int oracle_attention(long B, long h, long Lq, long Lk, long d_k, long d_v,
  */
 int oracle_attention_rows(long B, long h, long Lq, long Lk, long d_k, long d_v,
                           const double* q, const double* k, const double* v,
-                          int mask_flags, const int32_t* kv_lens,
+                          int mask_flags, const int32_t* kv_lens, long window,
                           long n_rows, const int64_t* rows, double* o_rows)
 {
-    if (B < 0 || h < 1 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1 || n_rows < 0) return -1;
+    if (B < 0 || h < 1 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1 || n_rows < 0 || window < -1)
+        return -1;
     if ((mask_flags & ORACLE_MASK_KEY_PADDING) && !kv_lens && B > 0) return -1;
     if ((mask_flags & ORACLE_MASK_CAUSAL) && Lq != Lk) return -1;
+    if (window >= 0 && Lq != Lk) return -1;
     for (long n = 0; n < n_rows; ++n) {
         const int64_t b = rows[3 * n], t = rows[3 * n + 1], i = rows[3 * n + 2];
         if (b < 0 || b >= B || t < 0 || t >= h || i < 0 || i >= Lq) return -1;
@@ -236,7 +249,7 @@ int oracle_attention_rows(long B, long h, long Lq, long Lk, long d_k, long d_v,
         } else {
 #pragma omp for schedule(dynamic, 4)
             for (long n = 0; n < n_rows; ++n)
-                attention_row(B, h, Lq, Lk, d_k, d_v, q, k, v, mask_flags, kv_lens,
+                attention_row(B, h, Lq, Lk, d_k, d_v, q, k, v, mask_flags, kv_lens, window,
                               rows[3 * n], rows[3 * n + 1], rows[3 * n + 2],
                               o_rows + n * d_v, NULL, NULL, logits, weights);
         }

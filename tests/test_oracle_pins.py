@@ -134,14 +134,15 @@ def pin_two_key_closed_form(O):
                                    atol=1e-300)
 
 
-def _legal(mask, lens, Lq, Lk, b):
+def _legal(mask, lens, Lq, Lk, b, window=None):
     L = Lk
     if mask & MASK_KEY_PADDING:
         L = min(max(int(lens[b]), 0), Lk)
     leg = np.zeros((Lq, Lk), dtype=bool)
     for i in range(Lq):
         for j in range(Lk):
-            leg[i, j] = (j < L) and (not (mask & MASK_CAUSAL) or j <= i)
+            leg[i, j] = (j < L) and (not (mask & MASK_CAUSAL) or j <= i) and \
+                (window is None or abs(i - j) <= window)
     return leg
 
 
@@ -315,13 +316,13 @@ def pin_torch_cross_check(O):
             np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
 
 
-def _brute(q, k, v, mask, lens):
+def _brute(q, k, v, mask, lens, window=None):
     """Pure-Python loops, written from the attention equation."""
     B, Lq, h, d = q.shape
     Lk, dv = k.shape[1], v.shape[3]
     out = np.zeros((B, Lq, h, dv))
     for b in range(B):
-        leg = _legal(mask, lens, Lq, Lk, b)
+        leg = _legal(mask, lens, Lq, Lk, b, window)
         for t in range(h):
             for i in range(Lq):
                 js = [j for j in range(Lk) if leg[i, j]]
@@ -362,12 +363,70 @@ def pin_rows_match_full(O):
         assert np.array_equal(sel[n], full[b, i, t])
 
 
+def pin_window_is_attention_over_the_neighbourhood(O):
+    """Restricted self-attention (Deep-reading page section 05): each output
+    row equals ordinary attention of that query over the keys within w
+    positions of it -- the neighbourhood sliced out of K and V, with the
+    padding length moved to the slice and causal cutting it at the query."""
+    rng = np.random.default_rng(21)
+    B, h, L, d = 2, 2, 17, 4
+    q, k, v = (_rand(rng, B, L, h, d) for _ in range(3))
+    lens = np.array([17, 9], dtype=np.int32)
+    for w in (0, 1, 3, 7):
+        for mask in (MASK_NONE, MASK_KEY_PADDING, MASK_CAUSAL, 3):
+            o = O.attention(q, k, v, mask=mask, kv_lens=lens, window=w)
+            for b in range(B):
+                for i in range(L):
+                    lo, hi = max(0, i - w), min(L, i + w + 1)
+                    if mask & MASK_CAUSAL:
+                        hi = min(hi, i + 1)
+                    n = hi - lo
+                    if mask & MASK_KEY_PADDING:
+                        n = min(max(int(lens[b]) - lo, 0), hi - lo)
+                    if n == 0:
+                        assert np.all(o[b, i] == 0.0)
+                        continue
+                    ref = O.attention(q[b:b + 1, i:i + 1], k[b:b + 1, lo:lo + n],
+                                      v[b:b + 1, lo:lo + n])
+                    np.testing.assert_allclose(o[b, i], ref[0, 0], rtol=1e-13, atol=1e-13)
+
+
+def pin_window_limits(O):
+    """A window covering every position is ordinary attention (bit for
+    bit); a window of 0 leaves each query its own position: O_i = V_i.  The
+    legal pairs of a row number min(i, w) + min(L - 1 - i, w) + 1, so the
+    work is O(r n d) with r = 2w + 1 (Deep-reading page section 05)."""
+    rng = np.random.default_rng(22)
+    B, h, L, d = 2, 3, 13, 4
+    q, k, v = (_rand(rng, B, L, h, d) for _ in range(3))
+    for mask in (MASK_NONE, MASK_CAUSAL):
+        assert np.array_equal(O.attention(q, k, v, mask=mask, window=L - 1),
+                              O.attention(q, k, v, mask=mask))
+    assert np.array_equal(O.attention(q, k, v, window=0), v)
+    for w in (1, 4):
+        _, p = O.attention(q, k, v, window=w, return_p=True)
+        for i in range(L):
+            assert np.all((p[:, :, i] != 0).sum(axis=-1) == min(i, w) + min(L - 1 - i, w) + 1)
+
+
+def pin_window_brute_force(O):
+    rng = np.random.default_rng(23)
+    for (B, h, L, d) in ((1, 1, 6, 2), (2, 2, 9, 4)):
+        q, k, v = (_rand(rng, B, L, h, d) for _ in range(3))
+        lens = rng.integers(0, L + 1, size=B).astype(np.int32)
+        for w in (0, 2, 5):
+            for mask in range(4):
+                np.testing.assert_allclose(O.attention(q, k, v, mask=mask, kv_lens=lens, window=w),
+                                           _brute(q, k, v, mask, lens, w), rtol=1e-12, atol=1e-12)
+
+
 PINS = [pin_worked_2x2_closed_form, pin_worked_2x2_printed_digits, pin_two_head_toy,
         pin_head_owns_column_block, pin_two_key_closed_form, pin_convex_combination,
         pin_masked_garbage_invariance, pin_shift_invariance, pin_uniform_weights,
         pin_single_key_and_empty, pin_permutation_equivariance, pin_scale_variance,
         pin_projection_identity, pin_torch_cross_check, pin_brute_force_tiny,
-        pin_rows_match_full]
+        pin_rows_match_full, pin_window_is_attention_over_the_neighbourhood,
+        pin_window_limits, pin_window_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -393,6 +452,8 @@ def test_brute_force_hypothesis(B, h, Lq, Lk, d, mask, seed):
 def test_rejects_bad_arguments():
     q = np.zeros((1, 4, 1, 2))
     k = np.zeros((1, 5, 1, 2))
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, k, window=2)                  # a window needs Lq == Lk
     with pytest.raises(ValueError):
         oracle.attention(q, k, k, mask=MASK_CAUSAL)          # causal needs Lq == Lk
     with pytest.raises(ValueError):
@@ -421,6 +482,8 @@ MUTANTS = {
     "matmul_dropped_term": ("for (long kk = 0; kk < K; ++kk) {",
                             "for (long kk = 0; kk + 1 < K; ++kk) {"),
     "padding_ignored": ("if ((mask_flags & ORACLE_MASK_KEY_PADDING) && j >= len_b) return 0;", ""),
+    "window_off_by_one": ("j > i + window)", "j >= i + window)"),
+    "window_one_sided": ("(j < i - window || j > i + window)", "(j > i + window)"),
     "empty_row_not_zero": ("for (long e = 0; e < d_v; ++e) o_row[e] = 0.0;\n        if (p_row)",
                            "for (long e = 0; e < d_v; ++e) o_row[e] = 1.0;\n        if (p_row)"),
 }
