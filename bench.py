@@ -239,11 +239,13 @@ def attention_sweep(dev, steps, warmup, workloads=None):
             s["o"] = torch.empty_like(s["q"])
             sets.append(s)
         fn = lambda s: mha.mha_forward(s["q"], s["k"], s["v"], mask=w.mask,
-                                       kv_lens=s["kv_lens"], out=s["o"])
+                                       kv_lens=s["kv_lens"], out=s["o"], window=w.window)
         sec = kernel_time(fn, sets, max(steps // 4, 2 * n_sets), warmup)
-        flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, inp["kv_lens"])
+        flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, inp["kv_lens"],
+                                           w.window)
         tf = flops / sec / 1e12
         out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L": w.Lq,
+                    "window": w.window,
                     "mask": "causal" if w.mask & 2 else "none", "us": round(sec * 1e6, 2),
                     "tflops": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)})
         log(f"  sweep {w.name}: {sec * 1e6:.1f} us, {tf:.1f} TFLOP/s "
@@ -394,6 +396,8 @@ def main():
     sweep = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup)
     heads = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup,
                                                        configs.head_sizes())
+    windowed = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup,
+                                                          configs.windows())
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inputs, args.cpu_seconds)
@@ -424,6 +428,7 @@ def main():
         "roofline": roofline,
         "attention_sweep": sweep,
         "head_size_sweep": heads,
+        "window_sweep": windowed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -99,6 +99,31 @@ int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v,
                 void* o, hipStream_t stream);
 
 /*
+ * mha_forward_windowed -- restricted self-attention: mha_forward with each
+ * query i seeing only the keys j with |i - j| <= window, a neighbourhood of
+ * r = 2*window + 1 positions centred on the query, so a layer costs
+ * O(r n d) instead of O(n^2 d) ([Deep] section 05, the complexity table,
+ * "Restricted self-attention"; [Slides] slide "Limitations and Future
+ * Work").  The band combines with mask_flags as their union (causal keeps
+ * i - window .. i).  Arguments as for mha_forward plus
+ *
+ *   window   half-width, >= 0 (0: each query sees its own position only);
+ *            values >= Lk restrict nothing.
+ *
+ * K and V rows below kv_lens[b] are data even where they lie outside some
+ * query's band, and must be finite, as for causal; rows at or past kv_lens[b]
+ * may hold any bits.
+ *
+ * Errors: MHA_ERR_INVALID_ARG also for window < 0 or Lq != Lk (query and
+ * key positions must lie on one axis); otherwise as mha_forward, with the
+ * same supported dtypes and head sizes.
+ */
+int mha_forward_windowed(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v,
+                         const void* q, const void* k, const void* v,
+                         int mask_flags, const int32_t* kv_lens, int window,
+                         void* o, hipStream_t stream);
+
+/*
  * mha_project_qkv -- the per-head projections of every head at once:
  *
  *     Q = X_q W^Q,  K = X_kv W^K,  V = X_kv W^V

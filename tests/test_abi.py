@@ -33,7 +33,8 @@ def L():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"mha_forward", "mha_project_qkv", "mha_out_proj",
-                                         "mha_self_attention_fused", "mha_status_string"}
+                                         "mha_self_attention_fused", "mha_forward_windowed",
+                                         "mha_status_string"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -140,3 +141,21 @@ def test_projection_size_limits(L):
     assert P(BF16, 1, 8, 8, 32768, 512, 64, 64, *([FAKE] * 8), None) == UNSUPPORTED
     O = L.mha_out_proj
     assert O(BF16, 1, 8, 512, 64, 32768, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_windowed_validation(L):
+    import ctypes
+    W = L.mha_forward_windowed
+    i, p = ctypes.c_int, ctypes.c_void_p
+    W.argtypes = [i, i, i, i, i, i, i, p, p, p, i, p, i, p, p]
+    # (dt, B, h, Lq, Lk, dk, dv, q, k, v, mask, lens, window, o, stream)
+    def call(**kw):
+        a = dict(dt=BF16, B=2, h=2, Lq=8, Lk=8, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, mask=0,
+                 lens=None, window=3, o=FAKE)
+        a.update(kw)
+        return W(*a.values(), None)
+    assert call(window=-1) == INVALID             # a window is >= 0
+    assert call(Lk=9) == INVALID                  # queries and keys on one axis
+    assert call(mask=1) == INVALID                # key padding needs lengths
+    assert call(dk=48, dv=48) == UNSUPPORTED
+    assert call(B=0) == OK

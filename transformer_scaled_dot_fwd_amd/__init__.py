@@ -8,6 +8,7 @@ library's HIP kernels; there is no CPU or PyTorch fallback, and a missing
 library raises at the first call.
 
     mha_forward(q, k, v, mask, kv_lens)          O = softmax(QK^T/sqrt(d_k) + M) V
+    mha_forward(..., window=w)                    the same over keys |i - j| <= w only
     mha_project_qkv(x_q, x_kv, w_q, w_k, w_v, h)  Q, K, V = X_q W^Q, X_kv W^K, X_kv W^V
     mha_out_proj(o, w_o)                          Y = Concat(heads) W^O
     mha_block(...)                                the three above in sequence
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
     i, p = ctypes.c_int, ctypes.c_void_p
     L.mha_forward.argtypes = [i, i, i, i, i, i, i, p, p, p, i, p, p, p]
     L.mha_forward.restype = i
+    L.mha_forward_windowed.argtypes = [i, i, i, i, i, i, i, p, p, p, i, p, i, p, p]
+    L.mha_forward_windowed.restype = i
     L.mha_project_qkv.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
     L.mha_project_qkv.restype = i
     L.mha_out_proj.argtypes = [i, i, i, i, i, i, p, p, p, p]
@@ -97,10 +100,11 @@ def _stream(device) -> int:
 
 
 def mha_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: int = MASK_NONE,
-                kv_lens: torch.Tensor | None = None, out: torch.Tensor | None = None
-                ) -> torch.Tensor:
+                kv_lens: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                window: int | None = None) -> torch.Tensor:
     """O = softmax(Q K^T / sqrt(d_k) + M) V; q [B,Lq,h,d_k], k [B,Lk,h,d_k],
-    v [B,Lk,h,d_v] -> o [B,Lq,h,d_v]."""
+    v [B,Lk,h,d_v] -> o [B,Lq,h,d_v].  window=w: restricted self-attention
+    (keys within w positions of each query; mha_forward_windowed)."""
     _check(q, "q")
     _check(k, "k", q.dtype)
     _check(v, "v", q.dtype)
@@ -126,11 +130,18 @@ def mha_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: int = M
         _check(out, "out", q.dtype)
         if out.shape != (B, Lq, h, dv):
             raise ValueError("out has the wrong shape")
-    rc = lib().mha_forward(_dtype_code(q), B, h, Lq, Lk, dk, dv, q.data_ptr(), k.data_ptr(),
-                           v.data_ptr(), int(mask), lens_ptr, out.data_ptr(),
-                           _stream(q.device))
+    if window is None:
+        rc = lib().mha_forward(_dtype_code(q), B, h, Lq, Lk, dk, dv, q.data_ptr(),
+                               k.data_ptr(), v.data_ptr(), int(mask), lens_ptr, out.data_ptr(),
+                               _stream(q.device))
+        name = "mha_forward"
+    else:
+        rc = lib().mha_forward_windowed(_dtype_code(q), B, h, Lq, Lk, dk, dv, q.data_ptr(),
+                                        k.data_ptr(), v.data_ptr(), int(mask), lens_ptr,
+                                        int(window), out.data_ptr(), _stream(q.device))
+        name = "mha_forward_windowed"
     if rc != 0:
-        raise MHAError(rc, "mha_forward")
+        raise MHAError(rc, name)
     return out
 
 

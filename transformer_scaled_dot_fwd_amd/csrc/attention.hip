@@ -45,6 +45,12 @@ namespace mha {
 // Software pipeline per wave: the score MFMAs of tile j+1 and the PV MFMAs
 // of tile j are interleaved with the softmax VALU work of tile j (for D =
 // 64, one MFMA per two exponentials).  Global loads run two tiles ahead.
+//
+// WIN: restricted self-attention ("Paper Deep Reading", section 05, the
+// complexity table): query i sees keys i - window .. i + window only.  The
+// workgroup streams just the tiles that overlap its queries' band, each
+// wave computes the tiles that overlap its own, and the band's edges are
+// masked like the other masks.
 // ---------------------------------------------------------------------------
 #ifndef ATTN_QB1_OCC
 #define ATTN_QB1_OCC 3
@@ -65,11 +71,11 @@ constexpr int attn_occupancy() {
     return D > 64 ? 2 : (QB == 1 ? ATTN_QB1_OCC : 2);
 }
 
-template <int D, int NW, int QB, bool PAD, bool CAUSAL>
+template <int D, int NW, int QB, bool PAD, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
-    int n_qtiles, float scale_log2e) {
+    int n_qtiles, float scale_log2e, int window) {
     static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head size");
     constexpr int NKK = D / 16;              // 16-wide k slices of q.k
     constexpr int DP = D < 32 ? 32 : D;      // d extent the PV blocks cover
@@ -128,13 +134,27 @@ __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_b
     if (PAD) kv_end = min(max(kv_lens[b], 0), Lk);
     int key_end = kv_end;
     if (CAUSAL) key_end = min(key_end, min(q0 + BM, Lq));
+    // The workgroup streams tiles t_first .. n_tiles - 1 (a band around its
+    // queries when WIN; window < Lk, so no sum below overflows).
+    int t_first = 0;
+    if (WIN) {
+        key_end = min(key_end, q0 + BM + window);
+        t_first = max(q0 - window, 0) / KT;
+    }
     const int n_tiles = (key_end + KT - 1) / KT;
+    const int n_loop = max(n_tiles - t_first, 0);
 
-    // Tiles this wave computes: none if it holds no query row; causal stops
-    // at the tile holding the wave's last query.
+    // Tiles this wave computes, w_first .. n_mine - 1: none if it holds no
+    // query row; causal stops at the tile holding the wave's last query; a
+    // band starts and stops a window away from the wave's queries.
     const int wq0 = q0 + WQ * wave;
     int n_mine = (wq0 < Lq) ? n_tiles : 0;
     if (CAUSAL) n_mine = min(n_mine, (wq0 + WQ + KT - 1) / KT);
+    int w_first = 0;
+    if (WIN) {
+        n_mine = min(n_mine, (min(kv_end, wq0 + WQ + window) + KT - 1) / KT);
+        w_first = max(wq0 - window, 0) / KT;
+    }
 
     const size_t rs = (size_t)H * D;  // elements between consecutive positions
     const bf16* qp = q + ((size_t)b * Lq * H + hh) * D;
@@ -230,7 +250,8 @@ __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_b
     // softmax(x - c) for any c), and bf16/fp32 have range to spare.
     auto mask_and_max = [&](int t, f32x16 (&S)[QB]) {
         const int k0 = t * KT;
-        const bool need_mask = (k0 + KT > kv_end) || (CAUSAL && k0 + KT - 1 > wq0);
+        const bool need_mask = (k0 + KT > kv_end) || (CAUSAL && k0 + KT - 1 > wq0) ||
+                               (WIN && (k0 < wq0 + WQ - 1 - window || k0 + KT - 1 > wq0 + window));
         if (need_mask) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -240,6 +261,7 @@ __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_b
                     const int key = k0 + acc_row(r, half);
                     bool legal = key < kv_end;
                     if (CAUSAL) legal = legal && key <= qi;
+                    if (WIN) legal = legal && key >= qi - window && key <= qi + window;
                     S[qb][r] = legal ? S[qb][r] : -INFINITY;
                 }
             }
@@ -292,17 +314,18 @@ __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_b
     // chunk is complete (chunk (qb, c) is done after pair 8qb + 4c + 3);
     // those not ready at their slot run after the last slot.  sched_barrier
     // fences keep the order.
-    auto tile_step = [&](int j, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
+    // j: the tile; jr = j - t_first: its place in the ring.
+    auto tile_step = [&](int j, int jr, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
         // LDS operands, issued up front: K of tile j+1, V^T of tile j.  P
         // chunk c covers keys 16c + {0..3, 8..11} (k = 0..7, lanes < 32) and
         // 16c + {4..7, 12..15} (k = 8..15, lanes >= 32); the matching V^T
         // operand: lane group g reads columns 32db + 16(g&1) + j of rows
         // base + 0..3 and base + 8..11, base = 16c + 4(g>>1).
-        const bf16* kt = sK + ((j + 1) % STAGES) * TILE + l32 * PITCH + 8 * half;
+        const bf16* kt = sK + ((jr + 1) % STAGES) * TILE + l32 * PITCH + 8 * half;
         bf16x8 ka[NKK];
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) ka[kk] = *(const bf16x8*)(kt + 16 * kk);
-        const bf16* vt = sV + (j % STAGES) * TILE;
+        const bf16* vt = sV + (jr % STAGES) * TILE;
         bf16x8 va[2][NDB];  // [chunk][d block]
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -364,33 +387,38 @@ __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_b
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // ---- prologue: tiles 0 and 1 into the ring, tiles 2 and 3 in flight ----
-    gload(0, 0);  // tiles 0 and 1 in flight together: one round trip
-    gload(1, 1);
+    // ---- prologue: the first two tiles into the ring, the next two in
+    // flight ----
+    gload(0, t_first);  // two tiles in flight together: one round trip
+    gload(1, t_first + 1);
     sstore(0, 0);
     sstore(1, 1);
-    gload(0, 2);
-    gload(1, 3);
+    gload(0, t_first + 2);
+    gload(1, t_first + 3);
     barrier_lds();
 
     f32x16 SA[QB], SB[QB];
-    if (0 < n_mine) scores(0, SA);
+    if (!WIN && 0 < n_mine) scores(0, SA);
 
     // ---- main loop, unrolled by two so the score buffers and the load
     // register sets alternate ----
-    auto iteration = [&](int j, int set, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
-        barrier_lds();  // tile j+1 is stored; everyone is done with tile j-1
-        sstore(set, (j + 2) % STAGES);
-        gload(set, j + 4);
+    auto iteration = [&](int jr, int set, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
+        barrier_lds();  // tile jr+1 is stored; everyone is done with tile jr-1
+        sstore(set, (jr + 2) % STAGES);
+        gload(set, t_first + jr + 4);
+        const int j = t_first + jr;
+        // A band that starts after the workgroup's first tile: the wave's
+        // first scores come straight from the ring.
+        if (WIN && j == w_first && j < n_mine) scores(jr % STAGES, Scur);
         // Past a wave's last tile, S_{j+1} reads a zero or unused stage and
         // is dropped.
-        if (j < n_mine) tile_step(j, Scur, Snext);
+        if (j >= w_first && j < n_mine) tile_step(j, jr, Scur, Snext);
     };
     // Both halves always run (an odd tail costs one barrier and loads that
     // read zeros), so the load/store pattern is the same on every trip.
-    for (int j = 0; j < n_tiles; j += 2) {
-        iteration(j, 0, SA, SB);
-        iteration(j + 1, 1, SB, SA);
+    for (int jr = 0; jr < n_loop; jr += 2) {
+        iteration(jr, 0, SA, SB);
+        iteration(jr + 1, 1, SB, SA);
     }
 
     // ---- epilogue: O = acc / l, or 0 for a row with no legal key ----
@@ -660,7 +688,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(const float* __restrict__ q,
                                                    float* __restrict__ o,
                                                    const int32_t* __restrict__ kv_lens, int B,
                                                    int H, int Lq, int Lk, int n_qtiles,
-                                                   float scale) {
+                                                   float scale, int window) {
     __shared__ float sK[F32_BN][D + 1];
     __shared__ float sV[F32_BN][D + 1];
     const int lane = threadIdx.x;
@@ -673,6 +701,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(const float* __restrict__ q,
     if (PAD) kv_end = min(max(kv_lens[b], 0), Lk);
     int key_end = kv_end;
     if (CAUSAL) key_end = min(key_end, min(q0 + F32_BM, Lq));
+    int k_start = 0;  // restricted attention (window >= 0): the band only
+    if (window >= 0) {
+        key_end = min(key_end, q0 + F32_BM + window);
+        k_start = max(q0 - window, 0) / F32_BN * F32_BN;
+    }
 
     const size_t rs = (size_t)H * D;
     const float* qp = q + ((size_t)b * Lq * H + hh) * D;
@@ -688,7 +721,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(const float* __restrict__ q,
     }
     float m_run = -INFINITY, l_run = 0.0f;
 
-    for (int k0 = 0; k0 < key_end; k0 += F32_BN) {
+    for (int k0 = k_start; k0 < key_end; k0 += F32_BN) {
         __syncthreads();
         for (int idx = lane; idx < F32_BN * D; idx += 64) {
             const int row = idx / D, col = idx % D;
@@ -703,6 +736,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(const float* __restrict__ q,
             const int key = k0 + j;
             if (key >= kv_end) break;
             if (CAUSAL && key > my_q) break;
+            if (window >= 0 && key > my_q + window) break;
+            if (window >= 0 && key < my_q - window) continue;
             float dot = 0.0f;
 #pragma unroll
             for (int c = 0; c < D; ++c) dot = __builtin_fmaf(qv[c], sK[j][c], dot);
@@ -740,25 +775,25 @@ hipError_t launch_f32_d(const AttnArgs& a, hipStream_t stream) {
     switch (a.mask) {
         case 0:
             hipLaunchKernelGGL((attn_fwd_f32<D, false, false>), grid, dim3(64), 0, stream, q, k, v,
-                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale);
+                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale, a.window);
             break;
         case 1:
             hipLaunchKernelGGL((attn_fwd_f32<D, true, false>), grid, dim3(64), 0, stream, q, k, v,
-                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale);
+                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale, a.window);
             break;
         case 2:
             hipLaunchKernelGGL((attn_fwd_f32<D, false, true>), grid, dim3(64), 0, stream, q, k, v,
-                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale);
+                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale, a.window);
             break;
         default:
             hipLaunchKernelGGL((attn_fwd_f32<D, true, true>), grid, dim3(64), 0, stream, q, k, v,
-                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale);
+                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale, a.window);
             break;
     }
     return hipGetLastError();
 }
 
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, bool WIN = false>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
     constexpr int BM = 32 * QB * NW;
     const int n_qtiles = (a.Lq + BM - 1) / BM;
@@ -771,20 +806,24 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
     bf16* o = (bf16*)a.o;
     switch (a.mask) {
         case 0:
-            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, false, false>), grid, block, 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, false, false, WIN>), grid, block, 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e,
+                               a.window);
             break;
         case 1:
-            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, true, false>), grid, block, 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, true, false, WIN>), grid, block, 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e,
+                               a.window);
             break;
         case 2:
-            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, false, true>), grid, block, 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, false, true, WIN>), grid, block, 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e,
+                               a.window);
             break;
         default:
-            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, true, true>), grid, block, 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e);
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, true, true, WIN>), grid, block, 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e,
+                               a.window);
             break;
     }
     return hipGetLastError();
@@ -831,6 +870,14 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     // Rows of at most 128 (256) keys: the whole K/V row in LDS at once.
     // Head sizes other than 64 run the long-row kernel at every length, 32
     // queries per wave.
+    if (a.window >= 0) {  // restricted attention: the long-row kernel's band variant
+        switch (a.D) {
+            case 16: return launch_bf16<16, ATTN_NW, 1, true>(a, stream);
+            case 32: return launch_bf16<32, ATTN_NW, 1, true>(a, stream);
+            case 128: return launch_bf16<128, 8, 1, true>(a, stream);
+            default: return launch_bf16<64, ATTN_NW, 1, true>(a, stream);
+        }
+    }
     switch (a.D) {
         case 16: return launch_bf16<16, ATTN_NW, 1>(a, stream);
         case 32: return launch_bf16<32, ATTN_NW, 1>(a, stream);

@@ -15,6 +15,7 @@ struct AttnArgs {
     const void* v;
     const int32_t* kv_lens;   // device, [B]; only read with key padding
     void* o;
+    int window = -1;          // restricted attention half-width; -1: none
 };
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);

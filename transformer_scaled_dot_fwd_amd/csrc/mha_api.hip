@@ -28,9 +28,14 @@ const char* mha_status_string(int status) {
     }
 }
 
-int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v, const void* q,
-                const void* k, const void* v, int mask_flags, const int32_t* kv_lens, void* o,
-                hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// mha_forward and mha_forward_windowed; window < 0: no restriction.
+int forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v, const void* q,
+            const void* k, const void* v, int mask_flags, const int32_t* kv_lens, int window,
+            void* o, hipStream_t stream) {
     if (dt != MHA_F32 && dt != MHA_BF16) return MHA_ERR_INVALID_ARG;
     if (B < 0 || h < 1 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1) return MHA_ERR_INVALID_ARG;
     if (mask_flags & ~(MHA_MASK_KEY_PADDING | MHA_MASK_CAUSAL)) return MHA_ERR_INVALID_ARG;
@@ -52,12 +57,32 @@ int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v, co
         return MHA_ERR_UNSUPPORTED;
 
     mha::AttnArgs a{B, h, Lq, Lk, d_k, mask_flags, q, k, v, kv_lens, o};
+    // A window of Lk or more restricts nothing; clamping it keeps the
+    // kernels' index sums far from overflow.
+    a.window = window < 0 ? -1 : (window < Lk ? window : Lk);
     if (dt == MHA_BF16) {
         if (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128) return MHA_ERR_UNSUPPORTED;
         return launch_status(mha::launch_attention_bf16(a, stream));
     }
     if (d_k != 8 && d_k != 16 && d_k != 32 && d_k != 64) return MHA_ERR_UNSUPPORTED;
     return launch_status(mha::launch_attention_f32(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_forward(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v, const void* q,
+                const void* k, const void* v, int mask_flags, const int32_t* kv_lens, void* o,
+                hipStream_t stream) {
+    return forward(dt, B, h, Lq, Lk, d_k, d_v, q, k, v, mask_flags, kv_lens, -1, o, stream);
+}
+
+int mha_forward_windowed(mha_dtype dt, int B, int h, int Lq, int Lk, int d_k, int d_v,
+                         const void* q, const void* k, const void* v, int mask_flags,
+                         const int32_t* kv_lens, int window, void* o, hipStream_t stream) {
+    if (window < 0 || Lq != Lk) return MHA_ERR_INVALID_ARG;
+    return forward(dt, B, h, Lq, Lk, d_k, d_v, q, k, v, mask_flags, kv_lens, window, o, stream);
 }
 
 int mha_project_qkv(mha_dtype dt, int B, int Lq, int Lk, int d_model, int h, int d_k, int d_v,

@@ -16,8 +16,21 @@ from .configs import MASK_CAUSAL, MASK_KEY_PADDING, Workload
 ELEM_BYTES = {"f32": 4, "bf16": 2}
 
 
-def legal_pairs(B, h, Lq, Lk, mask, kv_lens=None) -> int:
-    """Number of (b, head, i, j) with M_ij = 0."""
+def legal_pairs(B, h, Lq, Lk, mask, kv_lens=None, window=None) -> int:
+    """Number of (b, head, i, j) with M_ij = 0 (with a window w, only
+    |i - j| <= w; restricted attention, Deep-reading page section 05)."""
+    if window is not None:
+        lens = (np.clip(np.asarray(kv_lens, dtype=np.int64), 0, Lk)
+                if mask & MASK_KEY_PADDING else np.full(B, Lk, dtype=np.int64))
+        i = np.arange(Lq, dtype=np.int64)
+        lo = np.maximum(i - window, 0)
+        total = 0
+        for L in lens:
+            hi = np.minimum(i + window, int(L) - 1)
+            if mask & MASK_CAUSAL:
+                hi = np.minimum(hi, i)
+            total += int(np.maximum(hi - lo + 1, 0).sum())
+        return total * h
     if mask & MASK_KEY_PADDING:
         lens = np.clip(np.asarray(kv_lens, dtype=np.int64), 0, Lk)
     else:
@@ -34,8 +47,8 @@ def legal_pairs(B, h, Lq, Lk, mask, kv_lens=None) -> int:
     return total * h
 
 
-def attention_flops(B, h, Lq, Lk, d, mask, kv_lens=None) -> int:
-    return 4 * d * legal_pairs(B, h, Lq, Lk, mask, kv_lens)
+def attention_flops(B, h, Lq, Lk, d, mask, kv_lens=None, window=None) -> int:
+    return 4 * d * legal_pairs(B, h, Lq, Lk, mask, kv_lens, window)
 
 
 def attention_bytes(B, h, Lq, Lk, d, mask, kv_lens=None, dtype="bf16") -> int:

@@ -40,6 +40,7 @@ class Workload:
     block: bool = False      # full block: projections + attention + W^O
     d_model: int = 0
     description: str = ""
+    window: Optional[int] = None   # restricted attention half-width
 
     @property
     def seed(self) -> int:
@@ -107,11 +108,26 @@ def head_sizes():
     return out
 
 
+def windows():
+    """Restricted self-attention (Deep-reading page section 05, complexity
+    table): the base and big head shapes at L = 4096 (B = 6), each query
+    seeing the keys within w = 256 positions (r = 513), no mask and causal."""
+    out = []
+    n = 100
+    for h in (8, 16):
+        for mask, tag in ((MASK_NONE, "nomask"), (MASK_CAUSAL, "causal")):
+            n += 1
+            out.append(Workload(f"window_h{h}_L4096_w256_{tag}", n, B=6, h=h, Lq=4096, Lk=4096,
+                                d=64, dtype="bf16", mask=mask, window=256,
+                                description=f"h={h} L=4096 B=6 d=64 bf16 {tag}, window 256"))
+    return out
+
+
 def get(name: str) -> Workload:
     name = ALIASES.get(name, name)
     if name in CONFIGS:
         return CONFIGS[name]
-    for w in sweep() + head_sizes():
+    for w in sweep() + head_sizes() + windows():
         if w.name == name:
             return w
     raise KeyError(name)
