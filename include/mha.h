@@ -32,6 +32,7 @@
 #ifndef MHA_H
 #define MHA_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -193,6 +194,43 @@ int mha_self_attention_fused(mha_dtype dt, int B, int L, int d_model, int h, int
                              const void* x, const void* w_q, const void* w_k, const void* w_v,
                              int mask_flags, const int32_t* kv_lens, void* o,
                              hipStream_t stream);
+
+/*
+ * mha_decode -- one decoding step against a key/value cache: for every
+ * sequence b and head t, the newest position's query attends to the
+ * cache_lens[b] cached keys (positions 0 .. len - 1, which under the
+ * decoder's causal mask is every earlier position and itself):
+ *
+ *     o_b,t = softmax(q_b,t K_b,t^T / sqrt(d_k)) V_b,t
+ *
+ * ([Deep] section 04, attention equation; section 03 "Decoder layer", one
+ * position per step with the causal mask; beam search keeps one cache per
+ * beam, so beams are just more sequences).  The result equals mha_forward
+ * with Lq = 1, Lk = L_cache and MHA_MASK_KEY_PADDING with kv_lens =
+ * cache_lens, computed as a split over the cache (partial softmax states of
+ * 256-key chunks, merged in a fixed order, so it is deterministic) with fp32
+ * scores and weights.
+ *
+ *   q           [B, 1, h, d_k]        the step's queries
+ *   k_cache     [B, L_cache, h, d_k]  BLHD, as mha_forward's k; rows at or
+ *   v_cache     [B, L_cache, h, d_v]  past cache_lens[b] are never read
+ *   cache_lens  device int32 [B], clamped to [0, L_cache]; 0 gives o = 0
+ *   o           [B, 1, h, d_v]
+ *   workspace   caller-owned device memory of at least
+ *               mha_decode_workspace_bytes(B, h, L_cache, d_k) bytes,
+ *               16-byte aligned (fp32 partial states; its contents are
+ *               scratch, nothing needs clearing); workspace_bytes its size.
+ *               Calls that share a workspace must not run at the same time.
+ *
+ * Supported: MHA_BF16, d_k == d_v in {64, 128}, L_cache*h*d_k*2 < 2^31
+ * (B == 0 is a no-op); MHA_ERR_UNSUPPORTED otherwise.  A workspace that is
+ * NULL, misaligned or too small is MHA_ERR_INVALID_ARG.
+ */
+size_t mha_decode_workspace_bytes(int B, int h, int L_cache, int d_k);
+int mha_decode(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v,
+               const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* cache_lens, void* o,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* mha_status_string(int status);

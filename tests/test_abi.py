@@ -34,6 +34,7 @@ def L():
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"mha_forward", "mha_project_qkv", "mha_out_proj",
                                          "mha_self_attention_fused", "mha_forward_windowed",
+                                         "mha_decode", "mha_decode_workspace_bytes",
                                          "mha_status_string"}
 
 
@@ -158,4 +159,33 @@ def test_windowed_validation(L):
     assert call(Lk=9) == INVALID                  # queries and keys on one axis
     assert call(mask=1) == INVALID                # key padding needs lengths
     assert call(dk=48, dv=48) == UNSUPPORTED
+    assert call(B=0) == OK
+
+
+def test_decode_validation(L):
+    import ctypes
+    D = L.mha_decode
+    i, p = ctypes.c_int, ctypes.c_void_p
+    D.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, ctypes.c_size_t, p]
+    L.mha_decode_workspace_bytes.argtypes = [i, i, i, i]
+    L.mha_decode_workspace_bytes.restype = ctypes.c_size_t
+    need = L.mha_decode_workspace_bytes(4, 8, 1000, 64)
+    assert need == 4 * 8 * 4 * (64 + 2) * 4            # 4 chunks of 256 keys
+    assert L.mha_decode_workspace_bytes(4, 8, 0, 64) == 4 * 8 * 1 * 66 * 4
+    assert L.mha_decode_workspace_bytes(-1, 8, 10, 64) == 0
+    # (dt, B, h, L, dk, dv, q, k, v, lens, o, ws, ws_bytes, stream)
+    def call(**kw):
+        a = dict(dt=BF16, B=4, h=8, L=1000, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, lens=FAKE,
+                 o=FAKE, ws=FAKE, nb=need)
+        a.update(kw)
+        return D(*a.values(), None)
+    assert call(dt=9) == INVALID
+    assert call(L=-1) == INVALID
+    assert call(lens=None) == INVALID               # the cache lengths are required
+    assert call(ws=None) == INVALID
+    assert call(ws=FAKE + 4) == INVALID             # 16-byte alignment
+    assert call(nb=need - 4) == INVALID             # too small
+    assert call(dk=32, dv=32) == UNSUPPORTED
+    assert call(dk=64, dv=128) == UNSUPPORTED
+    assert call(dt=F32) == UNSUPPORTED
     assert call(B=0) == OK

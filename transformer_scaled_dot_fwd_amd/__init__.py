@@ -9,6 +9,7 @@ library raises at the first call.
 
     mha_forward(q, k, v, mask, kv_lens)          O = softmax(QK^T/sqrt(d_k) + M) V
     mha_forward(..., window=w)                    the same over keys |i - j| <= w only
+    mha_decode(q, k_cache, v_cache, cache_lens)   one decoding step against a K/V cache
     mha_project_qkv(x_q, x_kv, w_q, w_k, w_v, h)  Q, K, V = X_q W^Q, X_kv W^K, X_kv W^V
     mha_out_proj(o, w_o)                          Y = Concat(heads) W^O
     mha_block(...)                                the three above in sequence
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.mha_forward.restype = i
     L.mha_forward_windowed.argtypes = [i, i, i, i, i, i, i, p, p, p, i, p, i, p, p]
     L.mha_forward_windowed.restype = i
+    L.mha_decode.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, ctypes.c_size_t, p]
+    L.mha_decode.restype = i
+    L.mha_decode_workspace_bytes.argtypes = [i, i, i, i]
+    L.mha_decode_workspace_bytes.restype = ctypes.c_size_t
     L.mha_project_qkv.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
     L.mha_project_qkv.restype = i
     L.mha_out_proj.argtypes = [i, i, i, i, i, i, p, p, p, p]
@@ -142,6 +147,46 @@ def mha_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: int = M
         name = "mha_forward_windowed"
     if rc != 0:
         raise MHAError(rc, name)
+    return out
+
+
+def mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               cache_lens: torch.Tensor, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decoding step: q [B,1,h,d] against the caches k_cache, v_cache
+    [B,L_cache,h,d] with cache_lens (int32 [B]) valid keys -> o [B,1,h,d].
+    `workspace` (bytes, mha_decode_workspace_bytes) is allocated per call
+    from torch's caching allocator when not given."""
+    _check(q, "q")
+    _check(k_cache, "k_cache", q.dtype)
+    _check(v_cache, "v_cache", q.dtype)
+    _check(cache_lens, "cache_lens", torch.int32)
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be [B, 1, h, d]")
+    B, _, h, dk = q.shape
+    Lc = k_cache.shape[1]
+    dv = v_cache.shape[3]
+    if k_cache.shape != (B, Lc, h, dk) or v_cache.shape[:3] != (B, Lc, h):
+        raise ValueError("cache shape mismatch")
+    if cache_lens.shape != (B,):
+        raise ValueError(f"cache_lens must have shape ({B},)")
+    if out is None:
+        out = torch.empty((B, 1, h, dv), dtype=q.dtype, device=q.device)
+    else:
+        _check(out, "out", q.dtype)
+        if out.shape != (B, 1, h, dv):
+            raise ValueError("out has the wrong shape")
+    nbytes = int(lib().mha_decode_workspace_bytes(B, h, Lc, dk))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check(workspace, "workspace")
+    rc = lib().mha_decode(_dtype_code(q), B, h, Lc, dk, dv, q.data_ptr(), k_cache.data_ptr(),
+                          v_cache.data_ptr(), cache_lens.data_ptr(), out.data_ptr(),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream(q.device))
+    if rc != 0:
+        raise MHAError(rc, "mha_decode")
     return out
 
 

@@ -35,6 +35,22 @@ struct FusedArgs {
 hipError_t launch_self_attention_fused_bf16(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 
+// One decoding step: q [B, H, D] (one query per sequence and head) against
+// the caches k, v [B, L, H, D] with lens[b] valid keys (device int32 [B]);
+// o [B, H, D]; workspace: decode_workspace_bytes(B, H, L, D) bytes of fp32
+// partial states.  D in {64, 128}, bf16.
+struct DecodeArgs {
+    int B, H, L, D;
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* lens;
+    void* o;
+    void* workspace;
+};
+size_t decode_workspace_bytes(int B, int H, int L, int D);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
 // One GEMM problem Y[M, N] = X[M, K] W[K, N] (row-major).
 struct GemmProblem {
     const void* x;

@@ -142,6 +142,33 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model, const
     return launch_status(e);
 }
 
+size_t mha_decode_workspace_bytes(int B, int h, int L_cache, int d_k) {
+    if (B < 0 || h < 1 || L_cache < 0 || d_k < 1) return 0;
+    return mha::decode_workspace_bytes(B, h, L_cache, d_k);
+}
+
+int mha_decode(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v, const void* q,
+               const void* k_cache, const void* v_cache, const int32_t* cache_lens, void* o,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (dt != MHA_F32 && dt != MHA_BF16) return MHA_ERR_INVALID_ARG;
+    if (B < 0 || h < 1 || L_cache < 0 || d_k < 1 || d_v < 1) return MHA_ERR_INVALID_ARG;
+    if (B == 0) return MHA_OK;
+    if (!q || !o || !cache_lens || !workspace) return MHA_ERR_INVALID_ARG;
+    if (L_cache > 0 && (!k_cache || !v_cache)) return MHA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(o) || !aligned16(workspace) ||
+        (L_cache > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
+        return MHA_ERR_INVALID_ARG;
+    if (dt != MHA_BF16 || d_k != d_v || (d_k != 64 && d_k != 128)) return MHA_ERR_UNSUPPORTED;
+    if (workspace_bytes < mha::decode_workspace_bytes(B, h, L_cache, d_k))
+        return MHA_ERR_INVALID_ARG;
+    // One sequence's cache rows of one head are addressed with 32-bit byte
+    // offsets; one workgroup per (sequence, head, 256-key chunk).
+    if ((long long)L_cache * h * d_k * 2 >= (1LL << 31)) return MHA_ERR_UNSUPPORTED;
+    if ((long long)B * h * ((L_cache + 255) / 256 + 1) > INT_MAX) return MHA_ERR_UNSUPPORTED;
+    mha::DecodeArgs a{B, h, L_cache, d_k, q, k_cache, v_cache, cache_lens, o, workspace};
+    return launch_status(mha::launch_decode_bf16(a, stream));
+}
+
 int mha_self_attention_fused(mha_dtype dt, int B, int L, int d_model, int h, int d_k,
                              const void* x, const void* w_q, const void* w_k, const void* w_v,
                              int mask_flags, const int32_t* kv_lens, void* o,

@@ -123,11 +123,26 @@ def windows():
     return out
 
 
+def decodes():
+    """One decoding step against a K/V cache (Deep-reading page section 03,
+    one position per step; beam search with beam 4, section 06): 16
+    sequences x 4 beams = 64 cache rows of up to 4096 positions, lengths
+    U{2048..4096}, at the base (h=8) and big (h=16) head shapes, d=64.
+    Lq = 1: the step's query per head."""
+    out = []
+    for n, h in ((121, 8), (122, 16)):
+        out.append(Workload(f"decode_h{h}_B64_L4096", n, B=64, h=h, Lq=1, Lk=4096, d=64,
+                            dtype="bf16", mask=MASK_KEY_PADDING, lens=(2048, 4096),
+                            description=f"decode step: 64 caches (16 x beam 4), h={h}, "
+                                        f"d=64, L_cache=4096, lens U{{2048..4096}}"))
+    return out
+
+
 def get(name: str) -> Workload:
     name = ALIASES.get(name, name)
     if name in CONFIGS:
         return CONFIGS[name]
-    for w in sweep() + head_sizes() + windows():
+    for w in sweep() + head_sizes() + windows() + decodes():
         if w.name == name:
             return w
     raise KeyError(name)
