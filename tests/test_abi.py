@@ -170,7 +170,7 @@ def test_decode_validation(L):
     L.mha_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.mha_decode_workspace_bytes.restype = ctypes.c_size_t
     need = L.mha_decode_workspace_bytes(4, 8, 1000, 64)
-    assert need == 4 * 8 * 4 * (64 + 2) * 4            # 4 chunks of 256 keys
+    assert need == 4 * 8 * 2 * (64 + 2) * 4            # 2 chunks of 512 keys
     assert L.mha_decode_workspace_bytes(4, 8, 0, 64) == 4 * 8 * 1 * 66 * 4
     assert L.mha_decode_workspace_bytes(-1, 8, 10, 64) == 0
     # (dt, B, h, L, dk, dv, q, k, v, lens, o, ws, ws_bytes, stream)

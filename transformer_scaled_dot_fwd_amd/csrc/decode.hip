@@ -8,11 +8,13 @@
 // the whole cache, so the only mask left is the cache length.)  One query
 // per (sequence, head) makes this HBM-bound: each cached key costs 4 d bytes
 // of K and V for 4 d FLOPs.  The key range is therefore split over many
-// workgroups (split-K) that each stream a chunk of K/V at full bandwidth and
-// leave a partial softmax state (running max m, sum l, unnormalised acc),
-// and a second kernel merges a (sequence, head)'s partial states in a fixed
-// order (deterministic), the exact identity softmax(x) = softmax(x - c)
-// applied chunk by chunk.
+// workgroups (split-K): each streams one chunk of one sequence's cache, whole
+// key rows (every head of a position is contiguous in the cache, so a wave
+// reads one row as one contiguous block; per-head pieces of 128 bytes at the
+// row stride ran at a sixth of the rate), and leaves a partial softmax state
+// per head (running max m, sum l, unnormalised acc); a second kernel merges a
+// (sequence, head)'s partial states in a fixed order (deterministic), the
+// exact identity softmax(x) = softmax(x - c) applied chunk by chunk.
 //
 // Arithmetic is fp32 on the VALU: the scores stay in fp32 (no bf16 rounding
 // of p), and exp2 with log2(e) / sqrt(d_k) folded into q.
@@ -22,7 +24,7 @@
 namespace mha {
 namespace {
 
-constexpr int DEC_CHUNK = 256;   // keys per workgroup
+constexpr int DEC_CHUNK = 512;   // keys per workgroup (measured best of 128 .. 1024)
 constexpr int DEC_WAVES = 4;
 
 // One lane group of 8 lanes holds one key; lane s of the group holds d
@@ -47,132 +49,152 @@ __device__ __forceinline__ void dec_merge(DecState<D>& a, float m2, float l2, co
     a.m = m;
 }
 
-// Partial state of (sequence b, head t, chunk s) into part[((b H + t) S + s)
-// (D + 2) ..]: acc[0 .. D-1], m, l.
-template <int D>
+// Partial states of (sequence b, chunk s) for every head t, into
+// part[((b H + t) S + s) (D + 2) ..]: acc[0 .. D-1], m, l.
+//
+// A cached key's row holds all H heads contiguously (H * D * 2 bytes), so a
+// wave reads whole rows: lane group g (8 lanes) takes heads g, g + 8, ...
+// (HPL of them), lane sl of the group d elements E sl .. E sl + E - 1.  Wave
+// w streams keys k0 + w, k0 + w + 4, ... of the chunk, two rows ahead.
+template <int D, int HPL>
 __global__ __launch_bounds__(64 * DEC_WAVES) void decode_partial_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ lens, float* __restrict__ part, int H, int L, int n_split,
     float scale_log2e) {
     constexpr int E = D / 8;            // elements per lane
-    constexpr int NL = E / 8;           // 16-byte loads per lane per row
+    constexpr int NL = E / 8;           // 16-byte loads per lane per head row
     static_assert(D == 64 || D == 128, "head size");
-    __shared__ float red[DEC_WAVES][D + 2];
+    __shared__ float red[DEC_WAVES][8 * HPL][D + 2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int g = lane >> 3;            // key group: one key per round
+    const int g = lane >> 3;            // lane group: heads g + 8u
     const int sl = lane & 7;            // d slice
     const int w = (int)blockIdx.x;
     const int s = w % n_split;
-    const int bt = w / n_split;
-    const int b = bt / H, t = bt - (bt / H) * H;
+    const int b = w / n_split;
 
     const int len = min(max(lens[b], 0), L);
     const int k0 = s * DEC_CHUNK;
     const int k1 = min(k0 + DEC_CHUNK, len);
 
-    // q slice, pre-scaled to log2 units
-    float qv[E];
-    {
-        const bf16* qp = q + ((size_t)b * H + t) * D + E * sl;
+    // q slices of this lane's heads, pre-scaled to log2 units (heads past H
+    // read zeros and are never stored)
+    float qv[HPL][E];
 #pragma unroll
-        for (int u = 0; u < NL; ++u) {
-            const bf16x8 x = *(const bf16x8*)(qp + 8 * u);
+    for (int u = 0; u < HPL; ++u) {
+        const int t = g + 8 * u;
+        const bf16* qp = q + ((size_t)b * H + min(t, H - 1)) * D + E * sl;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qv[8 * u + e] = (float)x[e] * scale_log2e;
+        for (int c = 0; c < NL; ++c) {
+            const bf16x8 x = *(const bf16x8*)(qp + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[u][8 * c + e] = t < H ? (float)x[e] * scale_log2e : 0.0f;
         }
     }
 
-    // Key rows of (b, t): row j at byte j * H * D * 2; rows past the cache
-    // length read as zeros (never used).
+    // Rows of sequence b: key j at byte j * H * D * 2; rows at or past the
+    // cache length read as zeros (never used).
     const size_t rs = (size_t)H * D;
-    const bf16* kb = k + ((size_t)b * L * H + t) * D;
-    const bf16* vb = v + ((size_t)b * L * H + t) * D;
-    const uint32_t bytes = len > 0 ? (uint32_t)(((size_t)(len - 1) * rs + D) * 2) : 0u;
+    const bf16* kb = k + (size_t)b * L * rs;
+    const bf16* vb = v + (size_t)b * L * rs;
+    const uint32_t bytes = (uint32_t)((size_t)len * rs * 2);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, bytes);
 
-    DecState<D> st;
-    st.m = -INFINITY;
-    st.l = 0.0f;
+    DecState<D> st[HPL];
 #pragma unroll
-    for (int e = 0; e < E; ++e) st.acc[e] = 0.0f;
+    for (int u = 0; u < HPL; ++u) {
+        st[u].m = -INFINITY;
+        st[u].l = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) st[u].acc[e] = 0.0f;
+    }
 
-    // Round r: this lane group's key k0 + 32 r + 8 wave + g.  K/V rows of the
-    // next two rounds are in flight while a round is computed.
-    const int n_rounds = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
-    auto key_of = [&](int r) { return k0 + 32 * r + 8 * wave + g; };
-    auto offset = [&](int r) {
-        const int j = key_of(r);
-        return j < k1 ? (uint32_t)(((size_t)j * rs + E * sl) * 2) : OOB_OFFSET;
-    };
-    bf16x8 kbuf[3][NL], vbuf[3][NL];
+    const int n_rounds = k1 > k0 ? (k1 - k0 - wave + DEC_WAVES - 1) / DEC_WAVES : 0;
+    auto key_of = [&](int r) { return k0 + wave + DEC_WAVES * r; };
+    bf16x8 kbuf[3][HPL][NL], vbuf[3][HPL][NL];
     auto fetch = [&](int r, int slot) {
-        const uint32_t off = offset(r);
+        const int j = key_of(r);
+        const bool in = r < n_rounds;
 #pragma unroll
-        for (int u = 0; u < NL; ++u) {
-            kbuf[slot][u] = buffer_load16(kr, off + 16 * u);
-            vbuf[slot][u] = buffer_load16(vr, off + 16 * u);
+        for (int u = 0; u < HPL; ++u) {
+            const int t = g + 8 * u;
+            const uint32_t off = in && t < H ? (uint32_t)(((size_t)j * rs + (size_t)t * D + E * sl) * 2)
+                                             : OOB_OFFSET;
+#pragma unroll
+            for (int c = 0; c < NL; ++c) {
+                kbuf[slot][u][c] = buffer_load16(kr, off + 16 * c);
+                vbuf[slot][u][c] = buffer_load16(vr, off + 16 * c);
+            }
         }
     };
-    fetch(0, 0);
-    fetch(1, 1);
-    for (int r = 0; r < n_rounds; ++r) {
-        const int slot = r % 3;
-        fetch(r + 2, (r + 2) % 3);
-        float sc = 0.0f;
+    auto round = [&](int slot) {
 #pragma unroll
-        for (int u = 0; u < NL; ++u)
+        for (int u = 0; u < HPL; ++u) {
+            float sc = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sc = __builtin_fmaf(qv[8 * u + e], (float)kbuf[slot][u][e], sc);
-        // the full dot product in all 8 lanes of the group
-        sc += __shfl_xor(sc, 1);
-        sc += __shfl_xor(sc, 2);
-        sc += __shfl_xor(sc, 4);
-        if (key_of(r) < k1) {  // the same in the 8 lanes of a group
-            const float m = fmaxf(st.m, sc);
-            const float alpha = __builtin_amdgcn_exp2f(st.m - m);  // 0 while empty
-            const float p = __builtin_amdgcn_exp2f(sc - m);
-            st.l = st.l * alpha + p;
-#pragma unroll
-            for (int u = 0; u < NL; ++u)
+            for (int c = 0; c < NL; ++c)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    st.acc[8 * u + e] =
-                        __builtin_fmaf(p, (float)vbuf[slot][u][e], st.acc[8 * u + e] * alpha);
-            st.m = m;
+                    sc = __builtin_fmaf(qv[u][8 * c + e], (float)kbuf[slot][u][c][e], sc);
+            sc += __shfl_xor(sc, 1);  // the full dot product in the group's 8 lanes
+            sc += __shfl_xor(sc, 2);
+            sc += __shfl_xor(sc, 4);
+            const float m = fmaxf(st[u].m, sc);
+            const float alpha = __builtin_amdgcn_exp2f(st[u].m - m);  // 0 while empty
+            const float p = __builtin_amdgcn_exp2f(sc - m);
+            st[u].l = __builtin_fmaf(st[u].l, alpha, p);
+#pragma unroll
+            for (int c = 0; c < NL; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    st[u].acc[8 * c + e] =
+                        __builtin_fmaf(p, (float)vbuf[slot][u][c][e], st[u].acc[8 * c + e] * alpha);
+            st[u].m = m;
         }
+    };
+    // Rounds three at a time so the register slots are fixed.
+    fetch(0, 0);
+    fetch(1, 1);
+    for (int r = 0; r < n_rounds; r += 3) {
+        fetch(r + 2, 2);
+        round(0);
+        if (r + 1 >= n_rounds) break;
+        fetch(r + 3, 0);
+        round(1);
+        if (r + 2 >= n_rounds) break;
+        fetch(r + 4, 1);
+        round(2);
     }
 
-    // The 8 key groups of the wave (lanes sl, sl + 8, ..., same d slice),
-    // then the 4 waves through LDS, merged in a fixed order.
+    // The 4 waves through LDS, merged in a fixed order by wave 0.
 #pragma unroll
-    for (int x = 8; x < 64; x <<= 1) {
-        const float m2 = __shfl_xor(st.m, x), l2 = __shfl_xor(st.l, x);
-        float a2[E];
+    for (int u = 0; u < HPL; ++u) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) a2[e] = __shfl_xor(st.acc[e], x);
-        dec_merge<D>(st, m2, l2, a2);
-    }
-    if (lane < 8) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) red[wave][E * sl + e] = st.acc[e];
-        if (lane == 0) {
-            red[wave][D] = st.m;
-            red[wave][D + 1] = st.l;
+        for (int e = 0; e < E; ++e) red[wave][g + 8 * u][E * sl + e] = st[u].acc[e];
+        if (sl == 0) {
+            red[wave][g + 8 * u][D] = st[u].m;
+            red[wave][g + 8 * u][D + 1] = st[u].l;
         }
     }
     __syncthreads();
-    if (wave == 0 && lane < 8) {
-        for (int ww = 1; ww < DEC_WAVES; ++ww) dec_merge<D>(st, red[ww][D], red[ww][D + 1], &red[ww][E * sl]);
-        float* out = part + (size_t)w * (D + 2);
+    if (wave == 0) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) out[E * sl + e] = st.acc[e];
-        if (lane == 0) {
-            out[D] = st.m;
-            out[D + 1] = st.l;
+        for (int u = 0; u < HPL; ++u) {
+            const int t = g + 8 * u;
+            for (int ww = 1; ww < DEC_WAVES; ++ww)
+                dec_merge<D>(st[u], red[ww][t][D], red[ww][t][D + 1], &red[ww][t][E * sl]);
+            if (t < H) {
+                float* out = part + (((size_t)b * H + t) * n_split + s) * (D + 2);
+#pragma unroll
+                for (int e = 0; e < E; ++e) out[E * sl + e] = st[u].acc[e];
+                if (sl == 0) {
+                    out[D] = st[u].m;
+                    out[D + 1] = st[u].l;
+                }
+            }
         }
     }
 }
@@ -204,16 +226,16 @@ __global__ __launch_bounds__(64) void decode_merge_bf16(const float* __restrict_
     for (int c = 0; c < PER; ++c) o[(size_t)bt * D + 64 * c + lane] = (bf16)(acc[c] * inv);
 }
 
-// Chunks per (sequence, head); at least one, so an empty cache still writes
-// (zero) outputs.
+// Chunks per sequence; at least one, so an empty cache still writes (zero)
+// outputs.
 int n_splits(int L) { return L > DEC_CHUNK ? (L + DEC_CHUNK - 1) / DEC_CHUNK : 1; }
 
-template <int D>
+template <int D, int HPL>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     const int n_split = n_splits(a.L);
     const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
     float* part = (float*)a.workspace;
-    hipLaunchKernelGGL(decode_partial_bf16<D>, dim3((unsigned)((long)a.B * a.H * n_split)),
+    hipLaunchKernelGGL((decode_partial_bf16<D, HPL>), dim3((unsigned)((long)a.B * n_split)),
                        dim3(64 * DEC_WAVES), 0, stream, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, a.lens, part, a.H, a.L, n_split, sl2e);
     hipLaunchKernelGGL(decode_merge_bf16<D>, dim3((unsigned)((long)a.B * a.H)), dim3(64), 0,
@@ -227,8 +249,16 @@ size_t decode_workspace_bytes(int B, int H, int L, int D) {
     return (size_t)B * H * n_splits(L) * (D + 2) * sizeof(float);
 }
 
+// Heads per lane group: 8 groups cover up to 8 heads per pass.
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-    return a.D == 128 ? launch_decode_d<128>(a, stream) : launch_decode_d<64>(a, stream);
+    if (a.D == 128) {
+        if (a.H <= 8) return launch_decode_d<128, 1>(a, stream);
+        if (a.H <= 16) return launch_decode_d<128, 2>(a, stream);
+        return launch_decode_d<128, 4>(a, stream);
+    }
+    if (a.H <= 8) return launch_decode_d<64, 1>(a, stream);
+    if (a.H <= 16) return launch_decode_d<64, 2>(a, stream);
+    return launch_decode_d<64, 4>(a, stream);
 }
 
 }  // namespace mha

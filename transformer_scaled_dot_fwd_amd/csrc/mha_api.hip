@@ -161,10 +161,10 @@ int mha_decode(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v, const 
     if (dt != MHA_BF16 || d_k != d_v || (d_k != 64 && d_k != 128)) return MHA_ERR_UNSUPPORTED;
     if (workspace_bytes < mha::decode_workspace_bytes(B, h, L_cache, d_k))
         return MHA_ERR_INVALID_ARG;
-    // One sequence's cache rows of one head are addressed with 32-bit byte
-    // offsets; one workgroup per (sequence, head, 256-key chunk).
+    // One sequence's cache rows are addressed with 32-bit byte offsets; one
+    // workgroup per (sequence, chunk of the cache).
     if ((long long)L_cache * h * d_k * 2 >= (1LL << 31)) return MHA_ERR_UNSUPPORTED;
-    if ((long long)B * h * ((L_cache + 255) / 256 + 1) > INT_MAX) return MHA_ERR_UNSUPPORTED;
+    if ((long long)B * (L_cache / 64 + 1) > INT_MAX) return MHA_ERR_UNSUPPORTED;
     mha::DecodeArgs a{B, h, L_cache, d_k, q, k_cache, v_cache, cache_lens, o, workspace};
     return launch_status(mha::launch_decode_bf16(a, stream));
 }
