@@ -255,6 +255,43 @@ def attention_sweep(dev, steps, warmup, workloads=None):
     return out
 
 
+def decode_sweep(dev, steps, warmup):
+    """One decoding step against a K/V cache (mha_decode): HBM-bound, so
+    reported as algorithmic GB/s (the valid K/V rows, q, o and the lengths)
+    against the 8 TB/s peak, next to the TFLOP/s of its 4 d FLOPs per key."""
+    import torch
+    import transformer_scaled_dot_fwd_amd as mha
+    from workloads import accounting, configs
+    out = []
+    for w in configs.decodes():
+        inp = configs.make_inputs(w)
+        one = working_set_bytes([inp["q"], inp["k"], inp["v"], inp["q"]])
+        n_sets = max(2, min(16, math.ceil(ROTATE_BYTES / one)))
+        ws = torch.empty(int(mha.lib().mha_decode_workspace_bytes(w.B, w.h, w.Lk, w.d)),
+                         dtype=torch.uint8, device=dev)
+        sets = []
+        for _ in range(n_sets):
+            s = {k: v.to(dev) if v is not None else None for k, v in inp.items()}
+            s["o"] = torch.empty_like(s["q"])
+            sets.append(s)
+        fn = lambda s: mha.mha_decode(s["q"], s["k"], s["v"], s["kv_lens"], out=s["o"],
+                                      workspace=ws)
+        sec = kernel_time(fn, sets, max(steps // 4, 2 * n_sets), warmup)
+        lens = inp["kv_lens"]
+        nbytes = accounting.attention_bytes(w.B, w.h, 1, w.Lk, w.d, w.mask, lens, w.dtype)
+        flops = accounting.attention_flops(w.B, w.h, 1, w.Lk, w.d, w.mask, lens)
+        gbps = nbytes / sec / 1e9
+        out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L_cache": w.Lk,
+                    "us": round(sec * 1e6, 2), "gbps": round(gbps, 1),
+                    "frac_peak_hbm": round(gbps * 1e9 / PEAK_HBM_BYTES, 4),
+                    "tflops": round(flops / sec / 1e12, 2)})
+        log(f"  decode {w.name}: {sec * 1e6:.1f} us, {gbps:.0f} GB/s "
+            f"({100 * gbps * 1e9 / PEAK_HBM_BYTES:.1f}% of HBM peak)")
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, inputs, budget_s):
     """The fp64 oracle (as it stands) on a bounded sample of the same
     workload: the block over whole batch rows, repeated until about
@@ -398,6 +435,7 @@ def main():
                                                        configs.head_sizes())
     windowed = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup,
                                                           configs.windows())
+    decoded = None if args.no_sweep else decode_sweep(dev, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inputs, args.cpu_seconds)
@@ -429,6 +467,7 @@ def main():
         "attention_sweep": sweep,
         "head_size_sweep": heads,
         "window_sweep": windowed,
+        "decode_sweep": decoded,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
