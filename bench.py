@@ -79,7 +79,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough CPU-time budget of the oracle sample")
     ap.add_argument("--kernel-only", choices=["project_qkv", "attention", "out_proj",
-                                              "self_attention_fused", "copy"])
+                                              "self_attention_fused", "decode", "copy"])
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as three launches (projection, attention, W^O) even "
                          "where the fused self-attention kernel applies")
@@ -326,18 +326,28 @@ def cpu_baseline(w, inputs, budget_s):
 
 
 def kernel_only_attention(w, dev, args):
-    """mha_forward alone on an attention workload, for counter runs."""
+    """mha_forward (or, for a decode workload, mha_decode) alone on an
+    attention workload, for trace and counter runs."""
     import torch
     import transformer_scaled_dot_fwd_amd as mha
     from workloads import configs
-    if args.kernel_only != "attention":
-        raise SystemExit("attention workloads run the attention kernel only")
     inp = configs.make_inputs(w, dev)
     o = torch.empty_like(inp["q"])
-    for _ in range(args.steps):
-        mha.mha_forward(inp["q"], inp["k"], inp["v"], mask=w.mask, kv_lens=inp["kv_lens"], out=o)
+    if args.kernel_only == "decode":
+        if w.Lq != 1:
+            raise SystemExit("--kernel-only decode needs a decode workload")
+        ws = torch.empty(int(mha.lib().mha_decode_workspace_bytes(w.B, w.h, w.Lk, w.d)),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(args.steps):
+            mha.mha_decode(inp["q"], inp["k"], inp["v"], inp["kv_lens"], out=o, workspace=ws)
+    elif args.kernel_only == "attention":
+        for _ in range(args.steps):
+            mha.mha_forward(inp["q"], inp["k"], inp["v"], mask=w.mask, kv_lens=inp["kv_lens"],
+                            out=o, window=w.window)
+    else:
+        raise SystemExit("attention workloads run the attention (or decode) kernels only")
     torch.cuda.synchronize()
-    log(f"attention on {w.name}: {args.steps} launches")
+    log(f"{args.kernel_only} on {w.name}: {args.steps} launches")
 
 
 def main():
