@@ -17,6 +17,9 @@ pages it follows, is written in ``oracle.c``:
 * ``attention_rows`` -- the same definition for a sampled list of rows.
 * ``matmul``         -- Y = A W (the projections and W^O of MultiHead;
   slide "Multi-Head Attention").
+* ``layer_norm``, ``out_proj_post_norm`` -- LayerNorm(x + Sublayer(x)),
+  the post-norm residual output of the sub-layer (Deep-reading page section
+  03).
 * ``mha_block``      -- MultiHead(X_q, X_kv, X_kv) = Concat(heads) W^O with
   head t = Attention(X_q W_t^Q, X_kv W_t^K, X_kv W_t^V), head t owning column
   block t (paperglide two-head toy example).
@@ -96,6 +99,8 @@ class Oracle:
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_matmul.argtypes = [L, L, L, P, P, P]
         lib.oracle_matmul.restype = ctypes.c_int
+        lib.oracle_layer_norm.argtypes = [L, L, P, P, P, ctypes.c_double, P]
+        lib.oracle_layer_norm.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -174,6 +179,25 @@ class Oracle:
         self.lib.oracle_matmul(M, K, N, _ptr(a), _ptr(w), _ptr(y))
         return y
 
+    def layer_norm(self, z, gamma, beta, eps: float = 1e-6):
+        """Per-row layer normalisation of z [..., N] in fp64 (population
+        variance, gain gamma [N], bias beta [N], eps inside the root)."""
+        z, gamma, beta = _f64(z), _f64(gamma), _f64(beta)
+        N = z.shape[-1]
+        if gamma.shape != (N,) or beta.shape != (N,):
+            raise ValueError("gamma and beta must have shape (N,)")
+        zz = np.ascontiguousarray(z.reshape(-1, N))
+        out = np.zeros_like(zz)
+        if self.lib.oracle_layer_norm(zz.shape[0], N, _ptr(zz), _ptr(gamma), _ptr(beta),
+                                      float(eps), _ptr(out)) != 0:
+            raise ValueError("oracle_layer_norm rejected its arguments")
+        return out.reshape(z.shape)
+
+    def out_proj_post_norm(self, o, w_o, x, gamma, beta, eps: float = 1e-6):
+        """LayerNorm(x + Concat(heads) W^O): the attention sub-layer's output
+        with its residual connection, post-norm.  x [B, Lq, d_model]."""
+        return self.layer_norm(_f64(x) + self.out_proj(o, w_o), gamma, beta, eps)
+
     def project_qkv(self, x_q, x_kv, w_q, w_k, w_v, h: int):
         """Q = X_q W^Q, K = X_kv W^K, V = X_kv W^V, returned BLHD.
 
@@ -243,6 +267,14 @@ def project_qkv(*args, **kw):
 
 def out_proj(*args, **kw):
     return default().out_proj(*args, **kw)
+
+
+def layer_norm(*args, **kw):
+    return default().layer_norm(*args, **kw)
+
+
+def out_proj_post_norm(*args, **kw):
+    return default().out_proj_post_norm(*args, **kw)
 
 
 def mha_block(*args, **kw):

@@ -260,6 +260,36 @@ int oracle_attention_rows(long B, long h, long Lq, long Lk, long d_k, long d_v,
 }
 
 /*
+ * The sub-layer's post-norm output LayerNorm(x + Sublayer(x)), applied to a
+ * residual sum z = x + y already formed: for each row of z [M, N],
+ *   mu = (1/N) sum_n z_n,  var = (1/N) sum_n (z_n - mu)^2,
+ *   out_n = gamma_n (z_n - mu) / sqrt(var + eps) + beta_n.
+ * ([Deep] section 03, "Residual + LayerNorm", post-norm order; [Slides]
+ * slide "Encoder Architecture".  The pages name layer normalisation without
+ * writing it out: this is its standard per-row form over the d_model
+ * features, population variance, learnable gain and bias, eps inside the
+ * square root.)  Two passes over the row, left to right.
+ */
+int oracle_layer_norm(long M, long N, const double* z, const double* gamma,
+                      const double* beta, double eps, double* out)
+{
+    if (M < 0 || N < 1 || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+    for (long m = 0; m < M; ++m) {
+        const double* zm = z + m * N;
+        double mu = 0.0;
+        for (long n = 0; n < N; ++n) mu += zm[n];
+        mu /= (double)N;
+        double var = 0.0;
+        for (long n = 0; n < N; ++n) var += (zm[n] - mu) * (zm[n] - mu);
+        var /= (double)N;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (long n = 0; n < N; ++n) out[m * N + n] = gamma[n] * (zm[n] - mu) * inv + beta[n];
+    }
+    return 0;
+}
+
+/*
  * Y = A W, A [M, K], W [K, N], Y [M, N], all row-major fp64; a plain triple
  * loop.  This is every linear map of the multi-head block: the per-head
  * projections Q W^Q, K W^K, V W^V (all heads at once, W = [W_1 || ... ||

@@ -420,13 +420,73 @@ def pin_window_brute_force(O):
                                            _brute(q, k, v, mask, lens, w), rtol=1e-12, atol=1e-12)
 
 
+def pin_layer_norm_moments_and_invariance(O):
+    """With unit gain and zero bias (eps = 0) every output row has mean 0
+    and mean square 1; a positive scale and a shift of a row leave it
+    unchanged; gain and bias act per feature afterwards."""
+    rng = np.random.default_rng(31)
+    z = _rand(rng, 5, 12)
+    one, zero = np.ones(12), np.zeros(12)
+    u = O.layer_norm(z, one, zero, eps=0.0)
+    np.testing.assert_allclose(u.mean(axis=1), 0.0, atol=1e-14)
+    np.testing.assert_allclose((u * u).mean(axis=1), 1.0, atol=1e-13)
+    np.testing.assert_allclose(O.layer_norm(3.5 * z - 2.0, one, zero, eps=0.0), u, atol=1e-13)
+    g, b = _rand(rng, 12), _rand(rng, 12)
+    np.testing.assert_allclose(O.layer_norm(z, g, b, eps=0.0), g * u + b, atol=1e-13)
+
+
+def pin_layer_norm_closed_forms(O):
+    """Two features [a, c]: mean (a+c)/2, variance ((a-c)/2)^2, so the
+    outputs are +-(a-c)/2 / sqrt(((a-c)/2)^2 + eps).  A constant row has
+    variance 0 and gives the bias exactly."""
+    for a, c, eps in ((1.0, -3.0, 1e-6), (0.25, 0.5, 0.5), (7.0, 7.5, 2.0)):
+        h = (a - c) / 2.0
+        r = h / math.sqrt(h * h + eps)
+        out = O.layer_norm(np.array([[a, c]]), np.ones(2), np.zeros(2), eps=eps)
+        np.testing.assert_allclose(out, [[r, -r]], rtol=0, atol=1e-15)
+    beta = np.array([0.5, -1.25, 3.0])
+    out = O.layer_norm(np.full((2, 3), 4.0), np.array([2.0, 3.0, 4.0]), beta, eps=1e-6)
+    assert np.array_equal(out, np.stack([beta, beta]))
+
+
+def pin_layer_norm_torch_cross_check(O):
+    """Library cross-check: torch.nn.functional.layer_norm in fp64."""
+    rng = np.random.default_rng(32)
+    for (M, N, eps) in ((4, 16, 1e-6), (3, 512, 1e-5), (2, 7, 0.5)):
+        z, g, b = _rand(rng, M, N), _rand(rng, N), _rand(rng, N)
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(z), (N,), torch.from_numpy(g),
+                                             torch.from_numpy(b), eps).numpy()
+        np.testing.assert_allclose(O.layer_norm(z, g, b, eps=eps), ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_post_norm_special_cases(O):
+    """LayerNorm(x + Concat(heads) W^O): with W^O = 0 it is LayerNorm(x);
+    with x = 0 it is LayerNorm of the projection alone; with W^O = I and
+    heads = -x it is the bias (a zero row normalises to 0)."""
+    rng = np.random.default_rng(33)
+    B, L, h, d = 2, 3, 2, 4
+    dm = h * d
+    o, x = _rand(rng, B, L, h, d), _rand(rng, B, L, dm)
+    g, b = _rand(rng, dm), _rand(rng, dm)
+    np.testing.assert_allclose(O.out_proj_post_norm(o, np.zeros((dm, dm)), x, g, b),
+                               O.layer_norm(x, g, b), atol=1e-13)
+    w = _rand(rng, dm, dm)
+    y = np.einsum("blk,kn->bln", o.reshape(B, L, dm), w)
+    np.testing.assert_allclose(O.out_proj_post_norm(o, w, np.zeros((B, L, dm)), g, b),
+                               O.layer_norm(y, g, b), atol=1e-12)
+    out = O.out_proj_post_norm(-x.reshape(B, L, h, d), np.eye(dm), x, g, b)
+    assert np.array_equal(out, np.broadcast_to(b, out.shape))
+
+
 PINS = [pin_worked_2x2_closed_form, pin_worked_2x2_printed_digits, pin_two_head_toy,
         pin_head_owns_column_block, pin_two_key_closed_form, pin_convex_combination,
         pin_masked_garbage_invariance, pin_shift_invariance, pin_uniform_weights,
         pin_single_key_and_empty, pin_permutation_equivariance, pin_scale_variance,
         pin_projection_identity, pin_torch_cross_check, pin_brute_force_tiny,
         pin_rows_match_full, pin_window_is_attention_over_the_neighbourhood,
-        pin_window_limits, pin_window_brute_force]
+        pin_window_limits, pin_window_brute_force, pin_layer_norm_moments_and_invariance,
+        pin_layer_norm_closed_forms, pin_layer_norm_torch_cross_check,
+        pin_post_norm_special_cases]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -484,6 +544,10 @@ MUTANTS = {
     "padding_ignored": ("if ((mask_flags & ORACLE_MASK_KEY_PADDING) && j >= len_b) return 0;", ""),
     "window_off_by_one": ("j > i + window)", "j >= i + window)"),
     "window_one_sided": ("(j < i - window || j > i + window)", "(j > i + window)"),
+    "ln_unbiased_variance": ("var /= (double)N;", "var /= (double)(N - 1);"),
+    "ln_eps_outside_root": ("1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
+    "ln_no_bias": (" * inv + beta[n];", " * inv;"),
+    "ln_no_centering": ("var += (zm[n] - mu) * (zm[n] - mu);", "var += zm[n] * zm[n];"),
     "empty_row_not_zero": ("for (long e = 0; e < d_v; ++e) o_row[e] = 0.0;\n        if (p_row)",
                            "for (long e = 0; e < d_v; ++e) o_row[e] = 1.0;\n        if (p_row)"),
 }
