@@ -19,9 +19,12 @@ cost every step, is printed beside it.
 
 Printed: one JSON line with the throughput (algorithmic TFLOP/s of the
 block), the roofline of the dominant kernel (timed alone with HIP events, in
-the same rotation), an attention-only sweep at L >= 1024 for the base and
-big head shapes, and the fp64 CPU oracle timed on the host as a reported
-baseline.
+the same rotation), the sub-layer with its residual and post-norm
+(LayerNorm(x + MultiHead(x)), W^O fused with the normalisation: its own
+HBM roofline and the sub-layer step time), attention-only sweeps (L >= 1024
+at the base and big head shapes, other head sizes, restricted attention),
+the decoding step against a K/V cache, and the fp64 CPU oracle timed on the
+host as a reported baseline.
 
 Counter runs: ``--kernel-only NAME`` runs just one kernel (or a plain
 device copy of known size, ``copy``) so rocprofv3 --pmc can read its
@@ -51,6 +54,8 @@ KERNEL_SOURCES = {
                                          "fused.hip"),
     "project_qkv": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc", "gemm.hip"),
     "out_proj": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc", "gemm.hip"),
+    "out_proj_post_norm": os.path.join(ROOT, "transformer_scaled_dot_fwd_amd", "csrc",
+                                       "norm.hip"),
 }
 
 
@@ -79,7 +84,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough CPU-time budget of the oracle sample")
     ap.add_argument("--kernel-only", choices=["project_qkv", "attention", "out_proj",
-                                              "self_attention_fused", "decode", "copy"])
+                                              "self_attention_fused", "out_proj_post_norm",
+                                              "decode", "copy"])
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as three launches (projection, attention, W^O) even "
                          "where the fused self-attention kernel applies")
@@ -102,6 +108,7 @@ class Block:
             s["v"] = torch.empty_like(s["q"])
             s["o"] = torch.empty_like(s["q"])
             s["y"] = torch.empty((B, L, dm), dtype=torch.bfloat16, device=dev)
+            s["z"] = torch.empty_like(s["y"])
             self.sets.append(s)
         self.fused = False
 
@@ -115,6 +122,10 @@ class Block:
 
     def out_proj(self, s):
         self.mha.mha_out_proj(s["o"], s["w_o"], out=s["y"])
+
+    def out_proj_post_norm(self, s):
+        self.mha.mha_out_proj_post_norm(s["o"], s["w_o"], s["x"], s["gamma"], s["beta"],
+                                        out=s["z"])
 
     def self_attention_fused(self, s):
         return self.mha.mha_self_attention_fused(s["x"], s["w_q"], s["w_k"], s["w_v"],
@@ -131,6 +142,16 @@ class Block:
             self.project_qkv(s)
             self.attention(s)
         self.out_proj(s)
+
+    def sublayer_step(self, s):
+        """The attention sub-layer with its residual and post-norm:
+        LayerNorm(x + MultiHead(x, x, x))."""
+        if self.fused:
+            self.self_attention_fused(s)
+        else:
+            self.project_qkv(s)
+            self.attention(s)
+        self.out_proj_post_norm(s)
 
 
 def working_set_bytes(tensors) -> int:
@@ -377,7 +398,7 @@ def main():
     probe = Block(w, inputs, dev, 1)
     s0 = probe.sets[0]
     one = working_set_bytes([s0[k] for k in ("x", "w_q", "w_k", "w_v", "w_o", "q", "k", "v",
-                                             "o", "y")])
+                                             "o", "y", "z")])
     n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / one)))
     del probe
     blk = Block(w, inputs, dev, n_sets)
@@ -387,7 +408,8 @@ def main():
 
     if args.kernel_only:
         fns = {"project_qkv": blk.project_qkv, "attention": blk.attention,
-               "out_proj": blk.out_proj, "self_attention_fused": blk.self_attention_fused}
+               "out_proj": blk.out_proj, "self_attention_fused": blk.self_attention_fused,
+               "out_proj_post_norm": blk.out_proj_post_norm}
         if args.kernel_only == "copy":
             src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
             dst = torch.empty_like(src)
@@ -415,6 +437,7 @@ def main():
     step_kernels = (["self_attention_fused", "out_proj"] if blk.fused
                     else ["project_qkv", "attention", "out_proj"])
     names = step_kernels + (["project_qkv", "attention"] if blk.fused else [])
+    names.append("out_proj_post_norm")
     per = {}
     for name in names:
         fn = getattr(blk, name)
@@ -439,6 +462,26 @@ def main():
         b = work[name]["bytes"]
         kernels[name] = {"us": round(sec * 1e6, 3), "tflops": round(f / sec / 1e12, 1),
                          "gbps": round(b / sec / 1e9, 1), "in_step": name in step_kernels}
+
+    # ---- the sub-layer with its residual and post-norm (W^O, + x, LayerNorm
+    # in one kernel), an HBM-bound kernel: arithmetic intensity under the
+    # ridge point of 2.5e15 / 8e12 = 312 FLOP/B ----
+    pn = "out_proj_post_norm"
+    pn_bytes = work[pn]["bytes"]
+    sec_sub = time_steps(blk.sublayer_step, blk.sets, args.steps, args.warmup)
+    post_norm = {
+        "kernel": pn, "bound": "hbm", "us": round(per[pn] * 1e6, 3),
+        "achieved": round(pn_bytes / per[pn] / 1e9, 1), "peak": PEAK_HBM_BYTES / 1e9,
+        "unit": "GB/s", "frac": round(pn_bytes / per[pn] / PEAK_HBM_BYTES, 4),
+        "tflops": round(work[pn]["flops"] / per[pn] / 1e12, 1),
+        "intensity_flop_per_byte": round(work[pn]["flops"] / pn_bytes, 1),
+        "traffic": traffic_for(pn, w.name),
+        "vs_out_proj_gemm_us": round(per["out_proj"] * 1e6, 3),
+        "sublayer_step_us": round(sec_sub * 1e6, 3),
+        "sublayer_step": " -> ".join(step_kernels[:-1] + [pn]),
+    }
+    log(f"  sub-layer with post-norm: {sec_sub * 1e6:.2f} us per step; {pn} "
+        f"{per[pn] * 1e6:.2f} us, {post_norm['achieved']:.0f} GB/s")
 
     sweep = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup)
     heads = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup,
@@ -474,6 +517,7 @@ def main():
         "frac_peak_bf16": round(value * 1e12 / PEAK_BF16_FLOPS, 4),
         "kernels": kernels,
         "roofline": roofline,
+        "post_norm": post_norm,
         "attention_sweep": sweep,
         "head_size_sweep": heads,
         "window_sweep": windowed,

@@ -168,6 +168,42 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
                  const void* o, const void* w_o, void* y, hipStream_t stream);
 
 /*
+ * mha_out_proj_post_norm -- the attention sub-layer's output with its
+ * residual connection and layer normalisation, in post-norm order:
+ *
+ *     y = LayerNorm(x_res + Concat(head_1, ..., head_h) W^O)
+ *     LayerNorm(z)_j = gamma_j (z_j - mu) / sqrt(var + eps) + beta_j
+ *
+ * with mu and var the mean and the population variance (divisor d_model) of
+ * the row z ([Deep] section 03, residual connection and LayerNorm around each
+ * sub-layer, and section 04, MultiHead equation; [Slides] slide "Encoder
+ * Architecture").  The pages name the normalisation without its formula;
+ * this is the usual per-feature-vector form, eps inside the square root.
+ * One kernel: the product, the residual add and the statistics stay in fp32
+ * on chip; only y (bf16) is written.
+ *
+ *   o      [B, Lq, h, d_v] = [B*Lq, h*d_v]   the attention output (BLHD)
+ *   w_o    [h*d_v, d_model]
+ *   x_res  [B, Lq, d_model]                  the sub-layer's input x
+ *   gamma, beta [d_model]                    gain and bias
+ *   eps    >= 0, finite (1e-6 is the usual choice); with eps = 0 a row whose
+ *          residual sum is constant has var = 0 and normalises to NaN
+ *   y      [B, Lq, d_model]                  output: either x_res itself
+ *          (in-place update of the residual stream) or memory that overlaps
+ *          none of the inputs
+ *
+ * All pointers device, 16-byte aligned.  Supported: MHA_BF16; d_model in
+ * {256, 512, 1024}; h*d_v % 32 == 0 and h*d_v * d_model < 2^30.
+ * MHA_ERR_UNSUPPORTED otherwise (MHA_F32 included); MHA_ERR_INVALID_ARG
+ * for negative sizes, a NaN, negative or infinite eps, a NULL or
+ * misaligned pointer, or y partly overlapping x_res.  B*Lq == 0 is a no-op.
+ */
+int mha_out_proj_post_norm(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
+                           const void* o, const void* w_o, const void* x_res,
+                           const void* gamma, const void* beta, float eps, void* y,
+                           hipStream_t stream);
+
+/*
  * mha_self_attention_fused -- the Q/K/V projections and the attention of
  * every head of a self-attention layer in one launch, for rows of at most
  * 128 tokens:

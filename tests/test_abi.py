@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"mha_forward", "mha_project_qkv", "mha_out_proj",
                                          "mha_self_attention_fused", "mha_forward_windowed",
                                          "mha_decode", "mha_decode_workspace_bytes",
-                                         "mha_status_string"}
+                                         "mha_out_proj_post_norm", "mha_status_string"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -189,3 +189,29 @@ def test_decode_validation(L):
     assert call(dk=64, dv=128) == UNSUPPORTED
     assert call(dt=F32) == UNSUPPORTED
     assert call(B=0) == OK
+
+
+def test_post_norm_validation(L):
+    P = L.mha_out_proj_post_norm
+    # (dt, B, Lq, h, dv, d_model, o, w_o, x_res, gamma, beta, eps, y, stream)
+    def call(**kw):
+        a = dict(dt=BF16, B=2, Lq=8, h=8, dv=64, dm=512, o=FAKE, w=FAKE, x=FAKE, g=FAKE,
+                 b=FAKE, eps=1e-6, y=FAKE)
+        a.update(kw)
+        return P(*a.values(), None)
+    assert call(dt=5) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(h=0) == INVALID
+    assert call(eps=-1e-3) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(eps=float("inf")) == INVALID
+    assert call(g=None) == INVALID
+    assert call(b=FAKE + 8) == INVALID                 # 16-byte alignment
+    assert call(y=FAKE + 16) == INVALID                # partly over x_res
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(dm=384) == UNSUPPORTED                 # d_model in {256, 512, 1024}
+    assert call(dm=2048) == UNSUPPORTED
+    assert call(h=3, dv=16) == UNSUPPORTED             # h*d_v % 32
+    assert call(h=1024, dv=1024, dm=1024) == UNSUPPORTED  # W^O of 2^30 elements
+    assert call(B=0) == OK
+    assert call(Lq=0, o=None) == OK

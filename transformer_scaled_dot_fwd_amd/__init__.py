@@ -12,6 +12,7 @@ library raises at the first call.
     mha_decode(q, k_cache, v_cache, cache_lens)   one decoding step against a K/V cache
     mha_project_qkv(x_q, x_kv, w_q, w_k, w_v, h)  Q, K, V = X_q W^Q, X_kv W^K, X_kv W^V
     mha_out_proj(o, w_o)                          Y = Concat(heads) W^O
+    mha_out_proj_post_norm(o, w_o, x, g, b)       LayerNorm(x + Concat(heads) W^O)
     mha_block(...)                                the three above in sequence
 
 Tensors are CUDA (HIP) tensors, contiguous, all of one dtype (torch.bfloat16
@@ -66,6 +67,9 @@ def lib() -> ctypes.CDLL:
     L.mha_project_qkv.restype = i
     L.mha_out_proj.argtypes = [i, i, i, i, i, i, p, p, p, p]
     L.mha_out_proj.restype = i
+    L.mha_out_proj_post_norm.argtypes = [i, i, i, i, i, i, p, p, p, p, p, ctypes.c_float,
+                                         p, p]
+    L.mha_out_proj_post_norm.restype = i
     L.mha_self_attention_fused.argtypes = [i, i, i, i, i, i, p, p, p, p, i, p, p, p]
     L.mha_self_attention_fused.restype = i
     L.mha_status_string.argtypes = [i]
@@ -241,6 +245,37 @@ def mha_out_proj(o: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor | None = 
                             out.data_ptr(), _stream(o.device))
     if rc != 0:
         raise MHAError(rc, "mha_out_proj")
+    return out
+
+
+def mha_out_proj_post_norm(o: torch.Tensor, w_o: torch.Tensor, x_res: torch.Tensor,
+                           gamma: torch.Tensor, beta: torch.Tensor, eps: float = 1e-6,
+                           out: torch.Tensor | None = None) -> torch.Tensor:
+    """LayerNorm(x_res + Concat(head_1..head_h) W^O) with gain gamma and bias
+    beta over d_model; o [B,Lq,h,d_v], w_o [h*d_v, d_model], x_res
+    [B,Lq,d_model], gamma/beta [d_model].  ``out`` may be ``x_res`` itself
+    (in-place update of the residual stream)."""
+    _check(o, "o")
+    for t, n in ((w_o, "w_o"), (x_res, "x_res"), (gamma, "gamma"), (beta, "beta")):
+        _check(t, n, o.dtype)
+    B, Lq, h, dv = o.shape
+    dm = w_o.shape[1]
+    if w_o.shape != (h * dv, dm):
+        raise ValueError("w_o shape mismatch")
+    if x_res.shape != (B, Lq, dm) or gamma.shape != (dm,) or beta.shape != (dm,):
+        raise ValueError("x_res, gamma or beta shape mismatch")
+    if out is None:
+        out = torch.empty((B, Lq, dm), dtype=o.dtype, device=o.device)
+    else:
+        _check(out, "out", o.dtype)
+        if out.shape != (B, Lq, dm):
+            raise ValueError("out has the wrong shape")
+    rc = lib().mha_out_proj_post_norm(_dtype_code(o), B, Lq, h, dv, dm, o.data_ptr(),
+                                      w_o.data_ptr(), x_res.data_ptr(), gamma.data_ptr(),
+                                      beta.data_ptr(), float(eps), out.data_ptr(),
+                                      _stream(o.device))
+    if rc != 0:
+        raise MHAError(rc, "mha_out_proj_post_norm")
     return out
 
 

@@ -51,6 +51,21 @@ struct DecodeArgs {
 size_t decode_workspace_bytes(int B, int H, int L, int D);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// The attention sub-layer's output with its residual and post-norm:
+// out[M, N] = LayerNorm(x[M, N] + o[M, K] w[K, N]) with gain gamma[N], bias
+// beta[N]; N in {256, 512, 1024}, K % 32 == 0, bf16.
+struct PostNormArgs {
+    int M, N, K;
+    const void* o;
+    const void* w;
+    const void* x;
+    const void* gamma;
+    const void* beta;
+    float eps;
+    void* out;
+};
+hipError_t launch_out_proj_post_norm_bf16(const PostNormArgs& a, hipStream_t stream);
+
 // One GEMM problem Y[M, N] = X[M, K] W[K, N] (row-major).
 struct GemmProblem {
     const void* x;

@@ -142,6 +142,34 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model, const
     return launch_status(e);
 }
 
+int mha_out_proj_post_norm(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
+                           const void* o, const void* w_o, const void* x_res, const void* gamma,
+                           const void* beta, float eps, void* y, hipStream_t stream) {
+    if (dt != MHA_F32 && dt != MHA_BF16) return MHA_ERR_INVALID_ARG;
+    if (B < 0 || Lq < 0 || h < 1 || d_v < 1 || d_model < 1) return MHA_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return MHA_ERR_INVALID_ARG;  // NaN, negative, inf
+    const long long M = (long long)B * Lq;
+    if (M == 0) return MHA_OK;
+    const void* ptrs[] = {o, w_o, x_res, gamma, beta, y};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return MHA_ERR_INVALID_ARG;
+    // y may be x_res itself (the residual stream updated in place: each
+    // workgroup reads its rows of x_res before it writes them) but must not
+    // overlap it otherwise.
+    const size_t rows_bytes = (size_t)M * d_model * 2;
+    const char* yb = (const char*)y;
+    const char* xb = (const char*)x_res;
+    if (yb != xb && yb < xb + rows_bytes && xb < yb + rows_bytes) return MHA_ERR_INVALID_ARG;
+    if (dt != MHA_BF16) return MHA_ERR_UNSUPPORTED;
+    const long long K = (long long)h * d_v;
+    if (d_model != 256 && d_model != 512 && d_model != 1024) return MHA_ERR_UNSUPPORTED;
+    if (K % 32 != 0 || M > INT_MAX) return MHA_ERR_UNSUPPORTED;
+    // W^O and 32 rows of o are addressed with 32-bit byte offsets.
+    if (K * d_model * 2 >= (1LL << 31) || K * 64 >= (1LL << 31)) return MHA_ERR_UNSUPPORTED;
+    mha::PostNormArgs a{(int)M, d_model, (int)K, o, w_o, x_res, gamma, beta, eps, y};
+    return launch_status(mha::launch_out_proj_post_norm_bf16(a, stream));
+}
+
 size_t mha_decode_workspace_bytes(int B, int h, int L_cache, int d_k) {
     if (B < 0 || h < 1 || L_cache < 0 || d_k < 1) return 0;
     return mha::decode_workspace_bytes(B, h, L_cache, d_k);

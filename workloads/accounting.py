@@ -86,7 +86,15 @@ def workload_work(w: Workload, kv_lens=None) -> dict:
         out["project_qkv"] = {"flops": qkv_f, "bytes": qkv_b}
         out["out_proj"] = {"flops": gemm_flops(M, w.d_model, n),
                            "bytes": gemm_bytes(M, w.d_model, n, w.dtype)}
-    out["total_flops"] = sum(v["flops"] for v in out.values() if isinstance(v, dict))
+        # W^O with the residual add and the post-norm: the product's FLOPs
+        # (the normalisation adds O(M d_model), under 1%); bytes: O, W^O, the
+        # residual x, the output, gain and bias.
+        e = ELEM_BYTES[w.dtype]
+        out["out_proj_post_norm"] = {
+            "flops": gemm_flops(M, w.d_model, n),
+            "bytes": e * (M * n + n * w.d_model + 2 * M * w.d_model + 2 * w.d_model)}
+    out["total_flops"] = sum(v["flops"] for k, v in out.items()
+                             if isinstance(v, dict) and k != "out_proj_post_norm")
     if w.block:
         # The projections and the attention as one kernel: X and the weights
         # read once, O written once, Q/K/V never leave the chip.

@@ -9,7 +9,8 @@ geometry stand in for them (N(0, 1) components are the premise of the
 1/sqrt(d_k) argument in Deep-reading page section 04).
 
 Seeds: 1000 * config_number + tensor_number, tensor numbers q=0, k=1, v=2,
-x_q=3, w_q=4, w_k=5, w_v=6, w_o=7, x_kv=8, lens=9.
+x_q=3, w_q=4, w_k=5, w_v=6, w_o=7, x_kv=8, lens=9, gamma=10,
+beta=11.
 """
 from __future__ import annotations
 
@@ -153,7 +154,7 @@ def make_inputs(w: Workload, device="cpu") -> dict:
 
     Attention-only workloads: q, k, v (BLHD) and kv_lens.  Block workloads:
     x (the decoder input, used as both X_q and X_kv: self-attention),
-    w_q, w_k, w_v, w_o and kv_lens.  Weights are N(0, 1/d_model): the second
+    w_q, w_k, w_v, w_o, kv_lens, and gamma, beta of the post-norm.  Weights are N(0, 1/d_model): the second
     parameter of N(., .) is read as the variance.
     """
     s = w.seed
@@ -166,6 +167,10 @@ def make_inputs(w: Workload, device="cpu") -> dict:
         out["w_k"] = generate.normal((dm, w.h * w.d), s + 5, w.dtype, std)
         out["w_v"] = generate.normal((dm, w.h * w.d), s + 6, w.dtype, std)
         out["w_o"] = generate.normal((w.h * w.d, dm), s + 7, w.dtype, std)
+        # gain and bias of the post-norm LayerNorm: 1 + 0.1 N(0, 1), 0.1 N(0, 1)
+        out["gamma"] = (1.0 + generate.normal((dm,), s + 10, "f32", 0.1)).to(
+            generate.torch_dtype(w.dtype))
+        out["beta"] = generate.normal((dm,), s + 11, w.dtype, 0.1)
     else:
         out["q"] = generate.normal((w.B, w.Lq, w.h, w.d), s + 0, w.dtype)
         out["k"] = generate.normal((w.B, w.Lk, w.h, w.d), s + 1, w.dtype)
