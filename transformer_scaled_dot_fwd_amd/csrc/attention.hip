@@ -12,6 +12,8 @@
 // and running sum l, rescaling the partial output when m grows), which is
 // the exact identity softmax(x) = softmax(x - c) applied tile by tile; the
 // score matrix never leaves registers.
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -859,6 +861,21 @@ hipError_t launch_short_bf16(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Compute units of the current device, queried once per device (a lost
+// race only repeats the query).
+int device_cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 }  // namespace
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
@@ -866,7 +883,9 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     // rows up to 2048, run 32 queries per wave: twice the workgroups and
     // three per CU, which hides load latency and evens out the causal
     // triangle.  Longer rows run 64 queries per wave, halving the LDS reads
-    // per MFMA.
+    // per MFMA, where that pays: rows of 2048 and more whose workgroups (two
+    // per CU) fill at least 90% of their last round on the CUs; a partial
+    // last round leaves CUs idle, and 32 queries per wave finishes first.
     // Rows of at most 128 (256) keys: the whole K/V row in LDS at once.
     // Head sizes other than 64 run the long-row kernel at every length, 32
     // queries per wave.
@@ -888,6 +907,13 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     if (a.Lk <= 256) return launch_short_bf16<8>(a, stream);
     const bool causal = (a.mask & 2) != 0;  // AttnArgs::mask bit 1
     if (a.Lq <= 512 || (causal && a.Lq <= 2048)) return launch_bf16<64, ATTN_NW, 1>(a, stream);
+    if (!causal) {
+        const long wg = (long)a.B * a.H * ((a.Lq + 255) / 256);
+        const long slots = 2L * device_cu_count();
+        const long rounds = (wg + slots - 1) / slots;
+        if (a.Lq < 2048 || wg * 10 < rounds * slots * 9)
+            return launch_bf16<64, ATTN_NW, 1>(a, stream);
+    }
     return launch_bf16<64, ATTN_NW, 2>(a, stream);
 }
 
