@@ -59,6 +59,8 @@ __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
     static_assert(W_INSTR >= 1 && W_INSTR * 1024 * NM_WAVES == W_BYTES, "W load split");
     __shared__ __attribute__((aligned(1024))) char smem[nm_smem<NB>()];
     __shared__ float2 red[NM_WAVES][NM_BM];
+    constexpr int GB_BYTES = 2 * N > 1024 ? 2 * N : 1024;  // gamma, then beta, in LDS
+    __shared__ __attribute__((aligned(1024))) char s_gb[2 * GB_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -105,6 +107,20 @@ __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
         for (int u = 0; u < W_INSTR; ++u)
             load_lds16(wr, ws + 1024 * (wave + NM_WAVES * u), woff[u] + wk);
     };
+
+    // Gain and bias go to LDS by direct loads of wave 0, issued before any
+    // other load, so the first ring wait (and its barrier) covers them and
+    // the epilogue does not wait on global memory for them.
+    if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t gr = make_rsrc(gamma, (uint32_t)(N * 2));
+        const __amdgpu_buffer_rsrc_t br = make_rsrc(beta, (uint32_t)(N * 2));
+#pragma unroll
+        for (int u = 0; u < GB_BYTES / 1024; ++u) {
+            load_lds16(gr, lds_addr(s_gb) + 1024 * u, (uint32_t)(1024 * u + 16 * lane));
+            load_lds16(br, lds_addr(s_gb + GB_BYTES) + 1024 * u,
+                       (uint32_t)(1024 * u + 16 * lane));
+        }
+    }
 
     // The residual rows, prefetched whole (16 bytes per lane, consecutive
     // lanes along a row) while the product runs; rows past M read as zeros.
@@ -175,18 +191,18 @@ __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
 
     // ---- residual, row statistics, normalisation ----
     // Lane (l32, half) holds row m0 + l32 and features
-    // f(nb, r) = 32 NB wave + 32 nb + 8 (r / 4) + 4 half + r % 4.  The gain
-    // and bias of those features load while the residual tile goes through
-    // LDS (row layout, pitch OPITCH; the ring is free once every wave has
-    // passed the barrier) to the accumulator layout.
+    // f(nb, r) = 32 NB wave + 32 nb + 8 (r / 4) + 4 half + r % 4.  The
+    // residual tile goes through LDS (row layout, pitch OPITCH; the ring is
+    // free once every wave has passed the barrier) to the accumulator
+    // layout.
     const int f0 = 32 * NB * wave + 4 * half;
     bf16x4 gv[NB][4], bv[NB][4];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            gv[nb][rg] = *(const bf16x4*)(gamma + f0 + 32 * nb + 8 * rg);
-            bv[nb][rg] = *(const bf16x4*)(beta + f0 + 32 * nb + 8 * rg);
+            gv[nb][rg] = *(const bf16x4*)(s_gb + 2 * (f0 + 32 * nb + 8 * rg));
+            bv[nb][rg] = *(const bf16x4*)(s_gb + GB_BYTES + 2 * (f0 + 32 * nb + 8 * rg));
         }
     char* so = smem;
     barrier_lds();
