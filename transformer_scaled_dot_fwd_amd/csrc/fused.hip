@@ -178,9 +178,11 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
     // ---- Q, K, V to LDS as bf16, in the layouts the attention reads ----
     // Register group q (r = 4q .. 4q+3) of feature block fb holds features
     // 32 (fb & 1) + 8q + 4 half .. +3 of matrix fb / 2 for this lane's token.
-    // K and V rows at or past the row's length are stored as zeros: like
-    // the rows the attention kernels never load, whatever X holds there
-    // cannot reach the output.
+    // A half swap between lanes l and l + 32 (same token) gathers whole
+    // 16-byte chunks: groups 2p and 2p + 1 become chunk 4 (fb & 1) + 2p +
+    // half, written by one 16-byte store.  K and V rows at or past the row's
+    // length are stored as zeros: like the rows the attention kernels never
+    // load, whatever X holds there cannot reach the output.
     barrier_lds();  // every wave is done with the projection ring
     char* const sQ = smem;
     char* const sK = smem + FTILE;
@@ -199,13 +201,27 @@ __global__ __launch_bounds__(256, 2) void self_attention_fused_bf16(
             const bool clip = mat != 0 && m0 + 32 > kv_end;
             const bool keep = m < kv_end;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 f = {acc[j][mb][4 * q4], acc[j][mb][4 * q4 + 1],
-                                 acc[j][mb][4 * q4 + 2], acc[j][mb][4 * q4 + 3]};
-                bf16x4 v4 = __builtin_convertvector(f, bf16x4);
-                if (clip && !keep) v4 = bf16x4{};
-                const int chunk = 4 * (fb & 1) + q4;
-                *(bf16x4*)(dst + m * 128 + ((chunk ^ swz) << 4) + 8 * half) = v4;
+            for (int p2 = 0; p2 < 2; ++p2) {
+                bf16x4 v4[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int q4 = 2 * p2 + u;
+                    const f32x4 f = {acc[j][mb][4 * q4], acc[j][mb][4 * q4 + 1],
+                                     acc[j][mb][4 * q4 + 2], acc[j][mb][4 * q4 + 3]};
+                    v4[u] = __builtin_convertvector(f, bf16x4);
+                    if (clip && !keep) v4[u] = bf16x4{};
+                }
+                // Swap the upper half of group 2p with the lower half of
+                // group 2p + 1: lane l < 32 then holds group 2p of lanes l and
+                // l + 32 (the low and high 8 bytes of chunk 2p), lane l + 32
+                // group 2p + 1 of both (chunk 2p + 1).
+                const auto lo = __builtin_bit_cast(uint2, v4[0]);
+                const auto hi = __builtin_bit_cast(uint2, v4[1]);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
+                const uint4 c = {s0[0], s1[0], s0[1], s1[1]};
+                const int chunk = 4 * (fb & 1) + 2 * p2 + half;
+                *(uint4*)(dst + m * 128 + ((chunk ^ swz) << 4)) = c;
             }
         }
     }
