@@ -44,11 +44,14 @@ constexpr int nm_smem() {
     return ring > stage_out ? ring : stage_out;
 }
 
+// xres and out may be the same buffer (the residual stream updated in
+// place), so neither is declared __restrict__; each workgroup reads its rows
+// of xres before it writes them.
 template <int NB>
 __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
-    const bf16* __restrict__ o, const bf16* __restrict__ w, const bf16* __restrict__ xres,
-    const bf16* __restrict__ gamma, const bf16* __restrict__ beta, bf16* __restrict__ out,
-    int M, int K, float eps) {
+    const bf16* __restrict__ o, const bf16* __restrict__ w, const bf16* xres,
+    const bf16* __restrict__ gamma, const bf16* __restrict__ beta, bf16* out, int M, int K,
+    float eps) {
     constexpr int N = 256 * NB;                     // d_model
     constexpr int ST = nm_stages<NB>();
     constexpr int X_BYTES = NM_BM * NM_BK * 2;      // 2 KB
