@@ -192,11 +192,13 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
  *          (in-place update of the residual stream) or memory that overlaps
  *          none of the inputs
  *
- * All pointers device, 16-byte aligned.  Supported: MHA_BF16; d_model in
- * {256, 512, 1024}; h*d_v % 32 == 0 and h*d_v * d_model < 2^30.
- * MHA_ERR_UNSUPPORTED otherwise (MHA_F32 included); MHA_ERR_INVALID_ARG
- * for negative sizes, a NaN, negative or infinite eps, a NULL or
- * misaligned pointer, or y partly overlapping x_res.  B*Lq == 0 is a no-op.
+ * All pointers device, 16-byte aligned.  Supported: d_model in
+ * {256, 512, 1024} and B*Lq, h*d_v < 2^31; MHA_BF16 also needs h*d_v % 32 ==
+ * 0 and h*d_v * d_model < 2^30 (one kernel on MFMA); MHA_F32 (exact fp32
+ * FMAs, the accuracy path) takes any h*d_v.  MHA_ERR_UNSUPPORTED otherwise;
+ * MHA_ERR_INVALID_ARG for negative sizes, a NaN, negative or infinite eps,
+ * a NULL or misaligned pointer, or y partly overlapping x_res.  B*Lq == 0
+ * is a no-op.
  */
 int mha_out_proj_post_norm(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
                            const void* o, const void* w_o, const void* x_res,

@@ -208,7 +208,8 @@ def test_post_norm_validation(L):
     assert call(g=None) == INVALID
     assert call(b=FAKE + 8) == INVALID                 # 16-byte alignment
     assert call(y=FAKE + 16) == INVALID                # partly over x_res
-    assert call(dt=F32) == UNSUPPORTED
+    assert call(dt=F32, dm=384) == UNSUPPORTED         # fp32 too: d_model in {256, 512, 1024}
+    assert call(dt=F32, y=FAKE + 16) == INVALID        # overlap counted in 4-byte elements
     assert call(dm=384) == UNSUPPORTED                 # d_model in {256, 512, 1024}
     assert call(dm=2048) == UNSUPPORTED
     assert call(h=3, dv=16) == UNSUPPORTED             # h*d_v % 32

@@ -1,7 +1,7 @@
 """GPU parity of mha_out_proj_post_norm, the attention sub-layer's output
 with its residual connection and post-norm, LayerNorm(x + Concat(heads) W^O)
 ("Paper Deep Reading", section 03 residual + LayerNorm, section 04 MultiHead
-equation).  Compared with the fp64 oracle on the same bf16 inputs.
+equation).  Compared with the fp64 oracle on the same bf16 (or fp32) inputs.
 
 Inputs: o ~ N(0, 1) (attention outputs are convex combinations of V rows,
 of unit scale), W^O ~ N(0, 1/(h d_v)) so that the product has unit variance,
@@ -122,3 +122,26 @@ def test_empty_batch_is_a_no_op():
                                    beta.to(dev))
     torch.cuda.synchronize()
     assert y.shape == (0, 1, 512)
+
+
+# fp32 (the accuracy path, exact fp32 FMAs): any h*d_v, including inner
+# sizes that are not multiples of 32 or of the 256-wide k chunk.
+F32_SHAPES = [(1, 1, 8, 64, 512), (2, 37, 8, 64, 512), (3, 50, 4, 64, 256), (2, 45, 16, 64, 1024),
+              (1, 33, 3, 16, 256), (1, 20, 5, 100, 512)]
+
+
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: "B{}_L{}_h{}_dv{}_dm{}".format(*s))
+def test_post_norm_fp32_against_oracle(shape):
+    dev = device()
+    B, Lq, h, dv, dm = shape
+    say(f"case post_norm fp32 {shape}")
+    o, w_o, x, gamma, beta = (t.float() for t in make(B, Lq, h, dv, dm, 7500 + sum(shape)))
+    y = run(o, w_o, x, gamma, beta, dev)
+    assert y.dtype == torch.float32
+    check(y, oracle.out_proj_post_norm(o, w_o, x, gamma, beta, eps=1e-6), "f32",
+          f"post_norm fp32 {shape}")
+    xs = x.to(dev).clone()
+    mha.mha_out_proj_post_norm(o.to(dev), w_o.to(dev), xs, gamma.to(dev), beta.to(dev),
+                               eps=1e-6, out=xs)
+    torch.cuda.synchronize()
+    assert torch.equal(xs.cpu(), y.cpu())

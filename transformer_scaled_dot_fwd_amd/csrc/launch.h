@@ -53,7 +53,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
 // The attention sub-layer's output with its residual and post-norm:
 // out[M, N] = LayerNorm(x[M, N] + o[M, K] w[K, N]) with gain gamma[N], bias
-// beta[N]; N in {256, 512, 1024}, K % 32 == 0, bf16.
+// beta[N]; N in {256, 512, 1024}; bf16 (K % 32 == 0) or fp32.
 struct PostNormArgs {
     int M, N, K;
     const void* o;
@@ -65,6 +65,7 @@ struct PostNormArgs {
     void* out;
 };
 hipError_t launch_out_proj_post_norm_bf16(const PostNormArgs& a, hipStream_t stream);
+hipError_t launch_out_proj_post_norm_f32(const PostNormArgs& a, hipStream_t stream);
 
 // One GEMM problem Y[M, N] = X[M, K] W[K, N] (row-major).
 struct GemmProblem {

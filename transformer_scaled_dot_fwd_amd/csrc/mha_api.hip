@@ -156,17 +156,19 @@ int mha_out_proj_post_norm(mha_dtype dt, int B, int Lq, int h, int d_v, int d_mo
     // y may be x_res itself (the residual stream updated in place: each
     // workgroup reads its rows of x_res before it writes them) but must not
     // overlap it otherwise.
-    const size_t rows_bytes = (size_t)M * d_model * 2;
+    const size_t rows_bytes = (size_t)M * d_model * (dt == MHA_BF16 ? 2 : 4);
     const char* yb = (const char*)y;
     const char* xb = (const char*)x_res;
     if (yb != xb && yb < xb + rows_bytes && xb < yb + rows_bytes) return MHA_ERR_INVALID_ARG;
-    if (dt != MHA_BF16) return MHA_ERR_UNSUPPORTED;
     const long long K = (long long)h * d_v;
     if (d_model != 256 && d_model != 512 && d_model != 1024) return MHA_ERR_UNSUPPORTED;
-    if (K % 32 != 0 || M > INT_MAX) return MHA_ERR_UNSUPPORTED;
-    // W^O and 32 rows of o are addressed with 32-bit byte offsets.
-    if (K * d_model * 2 >= (1LL << 31) || K * 64 >= (1LL << 31)) return MHA_ERR_UNSUPPORTED;
+    if (K > INT_MAX || M > INT_MAX) return MHA_ERR_UNSUPPORTED;
     mha::PostNormArgs a{(int)M, d_model, (int)K, o, w_o, x_res, gamma, beta, eps, y};
+    if (dt == MHA_F32) return launch_status(mha::launch_out_proj_post_norm_f32(a, stream));
+    // bf16: the k step is 32, and W^O and 32 rows of o are addressed with
+    // 32-bit byte offsets.
+    if (K % 32 != 0) return MHA_ERR_UNSUPPORTED;
+    if (K * d_model * 2 >= (1LL << 31) || K * 64 >= (1LL << 31)) return MHA_ERR_UNSUPPORTED;
     return launch_status(mha::launch_out_proj_post_norm_bf16(a, stream));
 }
 

@@ -300,7 +300,126 @@ hipError_t launch_post_norm_d(const PostNormArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// fp32 (accuracy path): the same computation with exact fp32 FMAs on the
+// VALU.  A workgroup of 256 threads owns 16 whole rows; thread i holds
+// columns i, i + 256, ... (NPT of them) of every row.  O's rows stream
+// through LDS in chunks of 256 k; W^O is read one row of k at a time,
+// coalesced across the threads.  The row statistics are two passes (mean,
+// then squared deviations) reduced over the workgroup through LDS.
+// ---------------------------------------------------------------------------
+constexpr int NF_R = 16;    // rows per workgroup
+constexpr int NF_KC = 256;  // k chunk
+
+template <int NPT>
+__global__ __launch_bounds__(256) void out_proj_post_norm_f32(
+    const float* __restrict__ o, const float* __restrict__ w, const float* xres,
+    const float* __restrict__ gamma, const float* __restrict__ beta, float* out, int M, int K,
+    float eps) {
+    constexpr int N = 256 * NPT;
+    __shared__ float so[NF_R][NF_KC];
+    __shared__ float red[4][NF_R];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m0 = (int)blockIdx.x * NF_R;
+    const int rows = min(NF_R, M - m0);
+
+    float acc[NF_R][NPT];
+#pragma unroll
+    for (int r = 0; r < NF_R; ++r)
+#pragma unroll
+        for (int c = 0; c < NPT; ++c) acc[r][c] = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += NF_KC) {
+        const int kc = min(NF_KC, K - k0);
+        __syncthreads();  // the previous chunk is consumed
+        for (int i = tid; i < NF_R * NF_KC; i += 256) {
+            const int r = i / NF_KC, kk = i % NF_KC;
+            so[r][kk] = (r < rows && kk < kc) ? o[(size_t)(m0 + r) * K + k0 + kk] : 0.0f;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kc; ++kk) {
+            float wv[NPT];
+#pragma unroll
+            for (int c = 0; c < NPT; ++c) wv[c] = w[(size_t)(k0 + kk) * N + tid + 256 * c];
+#pragma unroll
+            for (int r = 0; r < NF_R; ++r)
+#pragma unroll
+                for (int c = 0; c < NPT; ++c) acc[r][c] = __builtin_fmaf(so[r][kk], wv[c], acc[r][c]);
+        }
+    }
+    // residual (rows past M stay zero and are never stored)
+#pragma unroll
+    for (int r = 0; r < NF_R; ++r)
+        if (r < rows)
+#pragma unroll
+            for (int c = 0; c < NPT; ++c) acc[r][c] += xres[(size_t)(m0 + r) * N + tid + 256 * c];
+
+    // Sum of v over each row of the workgroup: lanes, then the four waves.
+    auto row_sums = [&](const float (&v)[NF_R], float (&tot)[NF_R]) {
+#pragma unroll
+        for (int r = 0; r < NF_R; ++r) {
+            float x = v[r];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+            if (lane == 0) red[wave][r] = x;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NF_R; ++r) tot[r] = red[0][r] + red[1][r] + red[2][r] + red[3][r];
+        __syncthreads();
+    };
+    float part[NF_R], mu[NF_R], var[NF_R];
+#pragma unroll
+    for (int r = 0; r < NF_R; ++r) {
+        part[r] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NPT; ++c) part[r] += acc[r][c];
+    }
+    row_sums(part, mu);
+#pragma unroll
+    for (int r = 0; r < NF_R; ++r) {
+        mu[r] *= 1.0f / N;
+        part[r] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NPT; ++c) {
+            const float dz = acc[r][c] - mu[r];
+            part[r] = __builtin_fmaf(dz, dz, part[r]);
+        }
+    }
+    row_sums(part, var);
+#pragma unroll
+    for (int r = 0; r < NF_R; ++r) {
+        if (r >= rows) continue;
+        const float inv = 1.0f / sqrtf(var[r] * (1.0f / N) + eps);
+#pragma unroll
+        for (int c = 0; c < NPT; ++c) {
+            const int col = tid + 256 * c;
+            out[(size_t)(m0 + r) * N + col] =
+                __builtin_fmaf(gamma[col], (acc[r][c] - mu[r]) * inv, beta[col]);
+        }
+    }
+}
+
+template <int NPT>
+hipError_t launch_post_norm_f32_d(const PostNormArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.M + NF_R - 1) / NF_R));
+    hipLaunchKernelGGL((out_proj_post_norm_f32<NPT>), grid, dim3(256), 0, stream,
+                       (const float*)a.o, (const float*)a.w, (const float*)a.x,
+                       (const float*)a.gamma, (const float*)a.beta, (float*)a.out, a.M, a.K,
+                       a.eps);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_out_proj_post_norm_f32(const PostNormArgs& a, hipStream_t stream) {
+    switch (a.N) {
+        case 256: return launch_post_norm_f32_d<1>(a, stream);
+        case 512: return launch_post_norm_f32_d<2>(a, stream);
+        default: return launch_post_norm_f32_d<4>(a, stream);
+    }
+}
 
 hipError_t launch_out_proj_post_norm_bf16(const PostNormArgs& a, hipStream_t stream) {
     switch (a.N) {
