@@ -200,8 +200,11 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_partial_bf16(
 }
 
 // o_b,t from the n_split partial states of (b, t): one wave per (b, t), lane
-// e holding d elements e (and e + 64 for D = 128).  A sequence with no cached
-// key outputs 0.
+// e holding d elements e (and e + 64 for D = 128).  Lane s first reads chunk
+// s's (m, l) (64 chunks per pass), so the maximum and the chunk weights take
+// one memory round trip rather than one per chunk; the weighted sum then
+// walks the chunks in order (a fixed order: deterministic), its loads issued
+// eight chunks at a time.  A sequence with no cached key outputs 0.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_bf16(const float* __restrict__ part,
                                                          bf16* __restrict__ o, int n_split) {
@@ -210,17 +213,40 @@ __global__ __launch_bounds__(64) void decode_merge_bf16(const float* __restrict_
     const int bt = (int)blockIdx.x;
     const float* p = part + (size_t)bt * n_split * (D + 2);
     float mx = -INFINITY;
-    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, p[(size_t)s * (D + 2) + D]);
+    for (int s0 = 0; s0 < n_split; s0 += 64) {
+        const int s = s0 + lane;
+        mx = fmaxf(mx, s < n_split ? p[(size_t)s * (D + 2) + D] : -INFINITY);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     float l = 0.0f, acc[PER] = {};
     if (mx != -INFINITY) {
-        for (int s = 0; s < n_split; ++s) {
+        for (int s0 = 0; s0 < n_split; s0 += 64) {
+            const int s = s0 + lane;
             const float* ps = p + (size_t)s * (D + 2);
-            const float sc = __builtin_amdgcn_exp2f(ps[D] - mx);  // 0 for an empty chunk
-            l = __builtin_fmaf(ps[D + 1], sc, l);
+            // this lane's chunk weight (0 for an empty chunk or past the end)
+            const float sc = s < n_split ? __builtin_amdgcn_exp2f(ps[D] - mx) : 0.0f;
+            l = s < n_split ? __builtin_fmaf(ps[D + 1], sc, l) : l;
+            const int n = min(64, n_split - s0);
+            for (int j0 = 0; j0 < n; j0 += 8) {
+                float v[8][PER];
 #pragma unroll
-            for (int c = 0; c < PER; ++c) acc[c] = __builtin_fmaf(ps[64 * c + lane], sc, acc[c]);
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int c = 0; c < PER; ++c)
+                        v[j][c] = j0 + j < n ? p[(size_t)(s0 + j0 + j) * (D + 2) + 64 * c + lane]
+                                             : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float w = __shfl(sc, j0 + j);  // weight of chunk s0 + j0 + j
+#pragma unroll
+                    for (int c = 0; c < PER; ++c) acc[c] = __builtin_fmaf(v[j][c], w, acc[c]);
+                }
+            }
         }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
     for (int c = 0; c < PER; ++c) o[(size_t)bt * D + 64 * c + lane] = (bf16)(acc[c] * inv);
