@@ -424,6 +424,11 @@ __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_b
     }
 
     // ---- epilogue: O = acc / l, or 0 for a row with no legal key ----
+    // Each store is an 8-byte piece of a query's row, 32 rows per
+    // instruction.  Plain stores let L2 merge a row's pieces into whole
+    // lines; nontemporal stores (as the full-row writers elsewhere use) would
+    // send every piece to memory on its own, which measured 10-27% slower
+    // overall at 1024 keys and 5-9% at 4096.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = sum_halves(l_part[qb]);
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_b
                         bf16x4 out;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[qb][db][4 * rg + e] * inv);
-                        store_stream((bf16x4*)(orow + col), out);
+                        *(bf16x4*)(orow + col) = out;
                     }
                 }
         }
