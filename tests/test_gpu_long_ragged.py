@@ -2,8 +2,8 @@
 rows reach.
 
 The long-row attention kernel runs 64 queries per wave for non-causal rows
-of at least 2048 queries whose workgroups fill their last round on the CUs,
-and for causal rows longer than 2048; otherwise 32 per wave.  The sweep
+(longer than 512) whose workgroups fill their last round on the CUs, and
+for causal rows longer than 2048; otherwise 32 per wave.  The sweep
 shapes are multiples of 256, so these cases put ragged query and key tails
 (and cross-attention, Lq != Lk) into both variants.  The oracle evaluates
 sampled rows one by one (oracle_attention_rows) on the full-size inputs,

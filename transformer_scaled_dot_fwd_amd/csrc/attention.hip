@@ -888,9 +888,10 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     // rows up to 2048, run 32 queries per wave: twice the workgroups and
     // three per CU, which hides load latency and evens out the causal
     // triangle.  Longer rows run 64 queries per wave, halving the LDS reads
-    // per MFMA, where that pays: rows of 2048 and more whose workgroups (two
-    // per CU) fill at least 90% of their last round on the CUs; a partial
-    // last round leaves CUs idle, and 32 queries per wave finishes first.
+    // per MFMA, where that pays: non-causal rows whose workgroups (two per
+    // CU) fill at least 90% of their last round on the CUs, and causal rows
+    // above 2048; a partial last round leaves CUs idle, and 32 queries per
+    // wave finishes first.
     // Rows of at most 128 (256) keys: the whole K/V row in LDS at once.
     // Head sizes other than 64 run the long-row kernel at every length, 32
     // queries per wave.
@@ -916,8 +917,7 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
         const long wg = (long)a.B * a.H * ((a.Lq + 255) / 256);
         const long slots = 2L * device_cu_count();
         const long rounds = (wg + slots - 1) / slots;
-        if (a.Lq < 2048 || wg * 10 < rounds * slots * 9)
-            return launch_bf16<64, ATTN_NW, 1>(a, stream);
+        if (wg * 10 < rounds * slots * 9) return launch_bf16<64, ATTN_NW, 1>(a, stream);
     }
     return launch_bf16<64, ATTN_NW, 2>(a, stream);
 }
