@@ -20,12 +20,14 @@ than direct launches on a busy stream.
 
 Printed: one JSON line with the throughput (algorithmic TFLOP/s of the
 block), the roofline of the dominant kernel (timed alone with HIP events, in
-the same rotation), the sub-layer with its residual and post-norm
+the same rotation, as graphs of one launch per buffer set so the host's
+per-call cost cannot show), the sub-layer with its residual and post-norm
 (LayerNorm(x + MultiHead(x)), W^O fused with the normalisation: its own
 HBM roofline and the sub-layer step time), attention-only sweeps (L >= 1024
 at the base and big head shapes, other head sizes, restricted attention),
 the decoding step against a K/V cache, and the fp64 CPU oracle timed on the
-host as a reported baseline.
+host as a reported baseline.  The sweeps are timed as direct launches
+(each entry records the host's issue time per launch beside the GPU time).
 
 Counter runs: ``--kernel-only NAME`` runs just one kernel (or a plain
 device copy of known size, ``copy``) so rocprofv3 --pmc can read its
@@ -300,7 +302,8 @@ def attention_sweep(dev, steps, warmup, workloads=None):
             sets.append(s)
         fn = lambda s: mha.mha_forward(s["q"], s["k"], s["v"], mask=w.mask,
                                        kv_lens=s["kv_lens"], out=s["o"], window=w.window)
-        sec = kernel_time(fn, sets, max(steps // 4, 2 * n_sets), warmup)
+        host = {}
+        sec = time_eager(fn, sets, max(steps // 4, 2 * n_sets), max(warmup, n_sets), host)
         flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, inp["kv_lens"],
                                            w.window)
         tf = flops / sec / 1e12
@@ -308,6 +311,7 @@ def attention_sweep(dev, steps, warmup, workloads=None):
         out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L": w.Lq,
                     "window": w.window, "exps": exps,
                     "mask": "causal" if w.mask & 2 else "none", "us": round(sec * 1e6, 2),
+                    "host_us": round(host["s_per_step"] * 1e6, 2),
                     "tflops": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)})
         log(f"  sweep {w.name}: {sec * 1e6:.1f} us, {tf:.1f} TFLOP/s "
             f"({100 * tf * 1e12 / PEAK_BF16_FLOPS:.1f}% of bf16 peak)")
@@ -337,13 +341,15 @@ def decode_sweep(dev, steps, warmup):
             sets.append(s)
         fn = lambda s: mha.mha_decode(s["q"], s["k"], s["v"], s["kv_lens"], out=s["o"],
                                       workspace=ws)
-        sec = kernel_time(fn, sets, max(steps // 4, 2 * n_sets), warmup)
+        host = {}
+        sec = time_eager(fn, sets, max(steps // 4, 2 * n_sets), max(warmup, n_sets), host)
         lens = inp["kv_lens"]
         nbytes = accounting.attention_bytes(w.B, w.h, 1, w.Lk, w.d, w.mask, lens, w.dtype)
         flops = accounting.attention_flops(w.B, w.h, 1, w.Lk, w.d, w.mask, lens)
         gbps = nbytes / sec / 1e9
         out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L_cache": w.Lk,
-                    "us": round(sec * 1e6, 2), "gbps": round(gbps, 1),
+                    "us": round(sec * 1e6, 2), "host_us": round(host["s_per_step"] * 1e6, 2),
+                    "gbps": round(gbps, 1),
                     "frac_peak_hbm": round(gbps * 1e9 / PEAK_HBM_BYTES, 4),
                     "tflops": round(flops / sec / 1e12, 2)})
         log(f"  decode {w.name}: {sec * 1e6:.1f} us, {gbps:.0f} GB/s "
