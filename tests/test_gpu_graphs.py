@@ -1,8 +1,10 @@
-"""HIP graph capture of every entry point, as the benchmark runs them.
+"""HIP graph capture of every entry point.
 
-bench.py times its steps and sweeps as replays of captured graphs.  Each
-test here runs a call eagerly, captures the same call in a graph, and then
-replays the graph several times.  Before every replay the outputs are
+bench.py times each kernel alone as replays of captured graphs (one launch
+per buffer set) and reports graph replays of its step beside the direct
+launches; callers may capture the entry points too.  Each test here runs a
+call eagerly, captures the same call in a graph, and then replays the graph
+several times.  Before every replay the outputs are
 overwritten with NaN by eager work on the same stream, followed by a
 synchronisation.  Every replay must reproduce the eager outputs bit for bit
 (the kernels are deterministic, and no call records a memset or any other
