@@ -93,15 +93,22 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
 
 
-def _check(t: torch.Tensor, name: str, dtype=None) -> None:
+def _check(t: torch.Tensor, name: str, dtype=None, device=None, shape=None) -> None:
+    """t is a contiguous device tensor; of `dtype`, on `device` and of
+    `shape` where given (the library writes outputs by their shape, so a
+    smaller buffer must never reach it)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _stream(device) -> int:
@@ -115,8 +122,8 @@ def mha_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: int = M
     v [B,Lk,h,d_v] -> o [B,Lq,h,d_v].  window=w: restricted self-attention
     (keys within w positions of each query; mha_forward_windowed)."""
     _check(q, "q")
-    _check(k, "k", q.dtype)
-    _check(v, "v", q.dtype)
+    _check(k, "k", q.dtype, q.device)
+    _check(v, "v", q.dtype, q.device)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, L, h, d]")
     B, Lq, h, dk = q.shape
@@ -129,16 +136,12 @@ def mha_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: int = M
     if mask & MASK_KEY_PADDING:
         if kv_lens is None:
             raise ValueError("key padding needs kv_lens")
-        _check(kv_lens, "kv_lens", torch.int32)
-        if kv_lens.shape != (B,):
-            raise ValueError(f"kv_lens must have shape ({B},)")
+        _check(kv_lens, "kv_lens", torch.int32, q.device, (B,))
         lens_ptr = kv_lens.data_ptr()
     if out is None:
         out = torch.empty((B, Lq, h, dv), dtype=q.dtype, device=q.device)
     else:
-        _check(out, "out", q.dtype)
-        if out.shape != (B, Lq, h, dv):
-            raise ValueError("out has the wrong shape")
+        _check(out, "out", q.dtype, q.device, (B, Lq, h, dv))
     if window is None:
         rc = lib().mha_forward(_dtype_code(q), B, h, Lq, Lk, dk, dv, q.data_ptr(),
                                k.data_ptr(), v.data_ptr(), int(mask), lens_ptr, out.data_ptr(),
@@ -162,9 +165,9 @@ def mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     `workspace` (bytes, mha_decode_workspace_bytes) is allocated per call
     from torch's caching allocator when not given."""
     _check(q, "q")
-    _check(k_cache, "k_cache", q.dtype)
-    _check(v_cache, "v_cache", q.dtype)
-    _check(cache_lens, "cache_lens", torch.int32)
+    _check(k_cache, "k_cache", q.dtype, q.device)
+    _check(v_cache, "v_cache", q.dtype, q.device)
+    _check(cache_lens, "cache_lens", torch.int32, q.device)
     if q.dim() != 4 or q.shape[1] != 1:
         raise ValueError("q must be [B, 1, h, d]")
     B, _, h, dk = q.shape
@@ -177,14 +180,12 @@ def mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if out is None:
         out = torch.empty((B, 1, h, dv), dtype=q.dtype, device=q.device)
     else:
-        _check(out, "out", q.dtype)
-        if out.shape != (B, 1, h, dv):
-            raise ValueError("out has the wrong shape")
+        _check(out, "out", q.dtype, q.device, (B, 1, h, dv))
     nbytes = int(lib().mha_decode_workspace_bytes(B, h, Lc, dk))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     else:
-        _check(workspace, "workspace")
+        _check(workspace, "workspace", device=q.device)
     rc = lib().mha_decode(_dtype_code(q), B, h, Lc, dk, dv, q.data_ptr(), k_cache.data_ptr(),
                           v_cache.data_ptr(), cache_lens.data_ptr(), out.data_ptr(),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -201,7 +202,9 @@ def mha_project_qkv(x_q: torch.Tensor, x_kv: torch.Tensor, w_q: torch.Tensor,
     x_q [B,Lq,d_model], x_kv [B,Lk,d_model] (pass x_q again for
     self-attention), w_q/w_k [d_model, h*d_k], w_v [d_model, h*d_v]."""
     for t, n in ((x_q, "x_q"), (x_kv, "x_kv"), (w_q, "w_q"), (w_k, "w_k"), (w_v, "w_v")):
-        _check(t, n, x_q.dtype)
+        _check(t, n, x_q.dtype, x_q.device)
+    if x_q.dim() != 3 or x_kv.dim() != 3 or w_q.dim() != 2 or w_k.dim() != 2 or w_v.dim() != 2:
+        raise ValueError("x_q, x_kv must be [B, L, d_model] and the weights 2-D")
     B, Lq, dm = x_q.shape
     Lk = x_kv.shape[1]
     if x_kv.shape != (B, Lk, dm):
@@ -218,8 +221,9 @@ def mha_project_qkv(x_q: torch.Tensor, x_kv: torch.Tensor, w_q: torch.Tensor,
         v = torch.empty((B, Lk, h, dv), dtype=x_q.dtype, device=x_q.device)
     else:
         q, k, v = out
-        for t, n in ((q, "q"), (k, "k"), (v, "v")):
-            _check(t, n, x_q.dtype)
+        for t, n, shape in ((q, "q", (B, Lq, h, dk)), (k, "k", (B, Lk, h, dk)),
+                            (v, "v", (B, Lk, h, dv))):
+            _check(t, n, x_q.dtype, x_q.device, shape)
     rc = lib().mha_project_qkv(_dtype_code(x_q), B, Lq, Lk, dm, h, dk, dv, x_q.data_ptr(),
                                x_kv.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
                                q.data_ptr(), k.data_ptr(), v.data_ptr(), _stream(x_q.device))
@@ -232,7 +236,9 @@ def mha_out_proj(o: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor | None = 
                  ) -> torch.Tensor:
     """Y = Concat(head_1..head_h) W^O; o [B,Lq,h,d_v], w_o [h*d_v, d_model]."""
     _check(o, "o")
-    _check(w_o, "w_o", o.dtype)
+    _check(w_o, "w_o", o.dtype, o.device)
+    if o.dim() != 4 or w_o.dim() != 2:
+        raise ValueError("o must be [B, L, h, d_v] and w_o 2-D")
     B, Lq, h, dv = o.shape
     dm = w_o.shape[1]
     if w_o.shape != (h * dv, dm):
@@ -240,7 +246,7 @@ def mha_out_proj(o: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor | None = 
     if out is None:
         out = torch.empty((B, Lq, dm), dtype=o.dtype, device=o.device)
     else:
-        _check(out, "out", o.dtype)
+        _check(out, "out", o.dtype, o.device, (B, Lq, dm))
     rc = lib().mha_out_proj(_dtype_code(o), B, Lq, h, dv, dm, o.data_ptr(), w_o.data_ptr(),
                             out.data_ptr(), _stream(o.device))
     if rc != 0:
@@ -257,7 +263,9 @@ def mha_out_proj_post_norm(o: torch.Tensor, w_o: torch.Tensor, x_res: torch.Tens
     (in-place update of the residual stream)."""
     _check(o, "o")
     for t, n in ((w_o, "w_o"), (x_res, "x_res"), (gamma, "gamma"), (beta, "beta")):
-        _check(t, n, o.dtype)
+        _check(t, n, o.dtype, o.device)
+    if o.dim() != 4 or w_o.dim() != 2:
+        raise ValueError("o must be [B, L, h, d_v] and w_o 2-D")
     B, Lq, h, dv = o.shape
     dm = w_o.shape[1]
     if w_o.shape != (h * dv, dm):
@@ -267,9 +275,7 @@ def mha_out_proj_post_norm(o: torch.Tensor, w_o: torch.Tensor, x_res: torch.Tens
     if out is None:
         out = torch.empty((B, Lq, dm), dtype=o.dtype, device=o.device)
     else:
-        _check(out, "out", o.dtype)
-        if out.shape != (B, Lq, dm):
-            raise ValueError("out has the wrong shape")
+        _check(out, "out", o.dtype, o.device, (B, Lq, dm))
     rc = lib().mha_out_proj_post_norm(_dtype_code(o), B, Lq, h, dv, dm, o.data_ptr(),
                                       w_o.data_ptr(), x_res.data_ptr(), gamma.data_ptr(),
                                       beta.data_ptr(), float(eps), out.data_ptr(),
@@ -288,7 +294,9 @@ def mha_self_attention_fused(x: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tens
     None when the shape is outside the fused kernel (bf16, d_k = 64,
     L <= 128, d_model % 64 == 0): use the two-call path then."""
     for t, n in ((x, "x"), (w_q, "w_q"), (w_k, "w_k"), (w_v, "w_v")):
-        _check(t, n, x.dtype)
+        _check(t, n, x.dtype, x.device)
+    if x.dim() != 3 or w_q.dim() != 2 or w_k.dim() != 2 or w_v.dim() != 2:
+        raise ValueError("x must be [B, L, d_model] and the weights 2-D")
     B, L, dm = x.shape
     nq = w_q.shape[1]
     if w_q.shape != (dm, nq) or w_k.shape != (dm, nq) or w_v.shape != (dm, nq) or nq % h:
@@ -298,16 +306,12 @@ def mha_self_attention_fused(x: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tens
     if mask & MASK_KEY_PADDING:
         if kv_lens is None:
             raise ValueError("key padding needs kv_lens")
-        _check(kv_lens, "kv_lens", torch.int32)
-        if kv_lens.shape != (B,):
-            raise ValueError(f"kv_lens must have shape ({B},)")
+        _check(kv_lens, "kv_lens", torch.int32, x.device, (B,))
         lens_ptr = kv_lens.data_ptr()
     if out is None:
         out = torch.empty((B, L, h, dk), dtype=x.dtype, device=x.device)
     else:
-        _check(out, "out", x.dtype)
-        if out.shape != (B, L, h, dk):
-            raise ValueError("out has the wrong shape")
+        _check(out, "out", x.dtype, x.device, (B, L, h, dk))
     rc = lib().mha_self_attention_fused(_dtype_code(x), B, L, dm, h, dk, x.data_ptr(),
                                         w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
                                         int(mask), lens_ptr, out.data_ptr(), _stream(x.device))

@@ -866,12 +866,13 @@ hipError_t launch_short_bf16(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Compute units of the current device, queried once per device (a lost
-// race only repeats the query).
-int device_cu_count() {
+// Compute units of the device the stream belongs to (the current device for
+// the null stream), queried once per device (a lost race only repeats the
+// query).  Only the choice between two tilings depends on it.
+int device_cu_count(hipStream_t stream) {
     static std::atomic<int> cached[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
     int n = cached[dev].load(std::memory_order_relaxed);
     if (n > 0) return n;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -915,7 +916,7 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     if (a.Lq <= 512 || (causal && a.Lq <= 2048)) return launch_bf16<64, ATTN_NW, 1>(a, stream);
     if (!causal) {
         const long wg = (long)a.B * a.H * ((a.Lq + 255) / 256);
-        const long slots = 2L * device_cu_count();
+        const long slots = 2L * device_cu_count(stream);
         const long rounds = (wg + slots - 1) / slots;
         if (wg * 10 < rounds * slots * 9) return launch_bf16<64, ATTN_NW, 1>(a, stream);
     }
