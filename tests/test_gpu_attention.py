@@ -98,8 +98,10 @@ def sample_rows(B, h, L, n_random, seed):
     return np.array(rows, dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["c5", "sweep_h8_L1024_nomask", "sweep_h16_L2048_causal",
-                                  "sweep_h8_L4096_nomask"])
+# The long causal workload and every L >= 1024 sweep shape, at the timed
+# size and so in the launch variant the benchmark times (32 or 64 queries
+# per wave, causal or not).
+@pytest.mark.parametrize("name", ["c5"] + [w.name for w in configs.sweep()])
 def test_named_workload_sampled(name):
     dev = device()
     w = configs.get(name)
