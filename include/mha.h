@@ -246,7 +246,7 @@ int mha_self_attention_fused(mha_dtype dt, int B, int L, int d_model, int h, int
  * beam, so beams are just more sequences).  The result equals mha_forward
  * with Lq = 1, Lk = L_cache and MHA_MASK_KEY_PADDING with kv_lens =
  * cache_lens, computed as a split over the cache (partial softmax states of
- * 512-key chunks, merged in a fixed order, so it is deterministic) with fp32
+ * 1024-key chunks, merged in a fixed order, so it is deterministic) with fp32
  * scores and weights.
  *
  *   q           [B, 1, h, d_k]        the step's queries

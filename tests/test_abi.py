@@ -169,13 +169,15 @@ def test_decode_validation(L):
     D.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, ctypes.c_size_t, p]
     L.mha_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.mha_decode_workspace_bytes.restype = ctypes.c_size_t
-    need = L.mha_decode_workspace_bytes(4, 8, 1000, 64)
-    assert need == 4 * 8 * 2 * (64 + 2) * 4            # 2 chunks of 512 keys
+    need = L.mha_decode_workspace_bytes(4, 8, 2000, 64)
+    assert need == 4 * 8 * 2 * (64 + 2) * 4            # 2 chunks of 1024 keys
+    assert L.mha_decode_workspace_bytes(4, 8, 1024, 64) == 4 * 8 * 1 * 66 * 4
+    assert L.mha_decode_workspace_bytes(4, 8, 1025, 128) == 4 * 8 * 2 * 130 * 4
     assert L.mha_decode_workspace_bytes(4, 8, 0, 64) == 4 * 8 * 1 * 66 * 4
     assert L.mha_decode_workspace_bytes(-1, 8, 10, 64) == 0
     # (dt, B, h, L, dk, dv, q, k, v, lens, o, ws, ws_bytes, stream)
     def call(**kw):
-        a = dict(dt=BF16, B=4, h=8, L=1000, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, lens=FAKE,
+        a = dict(dt=BF16, B=4, h=8, L=2000, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, lens=FAKE,
                  o=FAKE, ws=FAKE, nb=need)
         a.update(kw)
         return D(*a.values(), None)

@@ -50,6 +50,21 @@ def test_decode_against_oracle(B, h, L, d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_decode_chunk_boundaries(d):
+    """Cache lengths on and next to multiples of 512 and 1024 keys, where a
+    sequence's split over the cache gains or loses a (partial) chunk."""
+    dev = device()
+    lens = torch.tensor([511, 512, 513, 1023, 1024, 1025, 2047, 2048, 2049, 3071, 3072, 3073],
+                        dtype=torch.int32)
+    B, h, L = len(lens), 8, 3073
+    say(f"case decode chunk boundaries d={d} L={L}")
+    q, k, v = make(B, h, L, d, 5400 + d)
+    o = decode(q, k, v, lens, dev)
+    check(o, oracle.attention(q, k, v, mask=PAD, kv_lens=lens), "bf16",
+          f"decode chunk boundaries d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_decode_never_reads_past_the_length_and_is_deterministic(d):
     dev = device()
     B, h, L = 4, 4, 700

@@ -24,8 +24,14 @@
 namespace mha {
 namespace {
 
-constexpr int DEC_CHUNK = 512;   // keys per workgroup (measured best of 128 .. 1024)
-constexpr int DEC_WAVES = 4;
+// Keys per workgroup and waves per workgroup: each wave streams every
+// DEC_WAVES-th key of its chunk (128 keys), two rows ahead.  A workgroup's
+// rate is bound by the bytes it has in flight, so eight waves per chunk of
+// 1024 keys beat four per chunk of 512 on mixed cache lengths (fewer partial
+// tail chunks, the same waves per key) and on short caches, and tie on full
+// ones; chunks of 256 to 2048 keys at four or eight waves were measured.
+constexpr int DEC_CHUNK = 1024;
+constexpr int DEC_WAVES = 8;
 
 // One lane group of 8 lanes holds one key; lane s of the group holds d
 // elements E s .. E s + E - 1 (E = D / 8) of q, of that key's K and V rows,
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_partial_bf16(
         round(2);
     }
 
-    // The 4 waves through LDS, merged in a fixed order by wave 0.
+    // The waves' states through LDS, merged in a fixed order by wave 0.
 #pragma unroll
     for (int u = 0; u < HPL; ++u) {
 #pragma unroll
