@@ -32,8 +32,9 @@ def decode(q, k, v, lens, dev, **kw):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+# h up to 8, 16 and 32 select 1, 2 and 4 heads per lane group.
 @pytest.mark.parametrize("B,h,L", [(5, 3, 1), (4, 8, 300), (3, 2, 1000), (9, 8, 4097),
-                                   (2, 16, 257)])
+                                   (2, 16, 257), (3, 24, 700), (4, 32, 2100)])
 def test_decode_against_oracle(B, h, L, d):
     dev = device()
     say(f"case decode d={d} B={B} h={h} L={L}")
