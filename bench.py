@@ -320,7 +320,35 @@ def attention_sweep(dev, steps, warmup, workloads=None):
     return out
 
 
-def decode_sweep(dev, steps, warmup):
+def copy_bandwidth(dev, nbytes=512 << 20, reps=20):
+    """A plain device-to-device copy of nbytes (torch's copy, a runtime blit
+    kernel), timed with HIP events on the current stream after a few untimed
+    copies: bytes read plus bytes written per second.  The practical HBM
+    ceiling the HBM-bound kernels are set against, next to the 8 TB/s spec."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / reps
+        best = sec if best is None else min(best, sec)
+    del src, dst
+    torch.cuda.empty_cache()
+    gbps = 2 * nbytes / best / 1e9
+    return {"bytes_per_copy": 2 * nbytes, "us": round(best * 1e6, 2), "gbps": round(gbps, 1),
+            "frac_peak_hbm": round(gbps * 1e9 / PEAK_HBM_BYTES, 4)}
+
+
+def decode_sweep(dev, steps, warmup, copy_gbps=None):
     """One decoding step against a K/V cache (mha_decode): HBM-bound, so
     reported as algorithmic GB/s (the valid K/V rows, q, o and the lengths)
     against the 8 TB/s peak, next to the TFLOP/s of its 4 d FLOPs per key."""
@@ -351,6 +379,7 @@ def decode_sweep(dev, steps, warmup):
                     "us": round(sec * 1e6, 2), "host_us": round(host["s_per_step"] * 1e6, 2),
                     "gbps": round(gbps, 1),
                     "frac_peak_hbm": round(gbps * 1e9 / PEAK_HBM_BYTES, 4),
+                    "frac_of_copy": round(gbps / copy_gbps, 4) if copy_gbps else None,
                     "tflops": round(flops / sec / 1e12, 2)})
         log(f"  decode {w.name}: {sec * 1e6:.1f} us, {gbps:.0f} GB/s "
             f"({100 * gbps * 1e9 / PEAK_HBM_BYTES:.1f}% of HBM peak)")
@@ -553,7 +582,12 @@ def main():
                                                        configs.head_sizes())
     windowed = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup,
                                                           configs.windows())
-    decoded = None if args.no_sweep else decode_sweep(dev, args.steps, args.warmup)
+    copy = copy_bandwidth(dev)
+    log(f"device copy: {copy['gbps']:.0f} GB/s read + written "
+        f"({100 * copy['frac_peak_hbm']:.1f}% of the HBM peak)")
+    post_norm["frac_of_copy"] = round(post_norm["achieved"] / copy["gbps"], 4)
+    decoded = None if args.no_sweep else decode_sweep(dev, args.steps, args.warmup,
+                                                      copy["gbps"])
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inputs, args.cpu_seconds)
@@ -585,6 +619,7 @@ def main():
         "frac_peak_bf16": round(value * 1e12 / PEAK_BF16_FLOPS, 4),
         "kernels": kernels,
         "roofline": roofline,
+        "hbm_copy": copy,
         "post_norm": post_norm,
         "attention_sweep": sweep,
         "head_size_sweep": heads,
