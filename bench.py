@@ -26,8 +26,11 @@ per-call cost cannot show), the sub-layer with its residual and post-norm
 HBM roofline and the sub-layer step time), attention-only sweeps (L >= 1024
 at the base and big head shapes, other head sizes, restricted attention),
 the decoding step against a K/V cache, and the fp64 CPU oracle timed on the
-host as a reported baseline.  The sweeps are timed as direct launches
-(each entry records the host's issue time per launch beside the GPU time).
+host as a reported baseline, and a plain device copy's bandwidth.  The
+sweeps are timed as direct launches (each entry records the host's issue
+time per launch beside the GPU time and the calls per timed region); they
+and the per-kernel figures report the median of five timed regions of at
+least 20 ms or 2 passes over the buffer sets.
 
 Counter runs: ``--kernel-only NAME`` runs just one kernel (or a plain
 device copy of known size, ``copy``) so rocprofv3 --pmc can read its
@@ -40,6 +43,7 @@ import dataclasses
 import hashlib
 import json
 import math
+import statistics
 import os
 import sys
 import time
@@ -89,6 +93,9 @@ def parse():
     ap.add_argument("--kernel-only", choices=["project_qkv", "attention", "out_proj",
                                               "self_attention_fused", "out_proj_post_norm",
                                               "decode", "copy"])
+    ap.add_argument("--warm-seconds", type=float, default=0.0,
+                    help="with --kernel-only: launch the kernel for this long first, "
+                    "untimed, so the traced --steps launches run at full clock")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as three launches (projection, attention, W^O) even "
                          "where the fused self-attention kernel applies")
@@ -260,13 +267,36 @@ def time_eager(step, sets, n, warmup, host=None):
     return e0.elapsed_time(e1) * 1e-3 / n
 
 
-def kernel_time(fn, sets, launches, warmup):
+def kernel_time(fn, sets, launches, warmup, repeats=5):
     """Average duration of one launch of fn, timed in graphs that each hold
     one launch per buffer set (so consecutive launches use different
-    buffers)."""
+    buffers): the median of `repeats` timed regions of at least `launches`
+    launches each."""
     g = capture(lambda s0: [fn(s) for s in sets], sets[:1])
     reps = max(1, math.ceil(launches / len(sets)))
-    return time_graphs(g, reps, max(1, warmup // len(sets))) / len(sets)
+    time_graphs(g, reps, max(1, warmup // len(sets)))
+    return statistics.median(time_graphs(g, reps, 0) / len(sets) for _ in range(repeats))
+
+
+def time_median(fn, sets, warmup, host=None, min_calls=0, min_sec=0.02, repeats=5):
+    """Seconds per call of fn(sets[i % len(sets)]) launched directly on the
+    stream: after `warmup` untimed calls, `repeats` timed regions, each of at
+    least min_calls calls and at least min_sec of GPU time (sized from a
+    first timed pass over the sets); the median region.  With `host`, the
+    median host issue time per call as well."""
+    est = time_eager(fn, sets, len(sets), warmup)
+    n = max(min_calls, len(sets), math.ceil(min_sec / max(est, 1e-9)))
+    n = math.ceil(n / len(sets)) * len(sets)
+    runs = []
+    for _ in range(repeats):
+        h = {}
+        runs.append((time_eager(fn, sets, n, 0, h), h["s_per_step"]))
+    runs.sort()
+    sec, host_s = runs[len(runs) // 2]
+    if host is not None:
+        host["s_per_step"] = host_s
+        host["calls"] = n
+    return sec
 
 
 def traffic_for(name, launches_key):
@@ -303,7 +333,7 @@ def attention_sweep(dev, steps, warmup, workloads=None):
         fn = lambda s: mha.mha_forward(s["q"], s["k"], s["v"], mask=w.mask,
                                        kv_lens=s["kv_lens"], out=s["o"], window=w.window)
         host = {}
-        sec = time_eager(fn, sets, max(steps // 4, 2 * n_sets), max(warmup, n_sets), host)
+        sec = time_median(fn, sets, max(warmup, n_sets), host, min_calls=max(steps // 4, 2 * n_sets))
         flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, inp["kv_lens"],
                                            w.window)
         tf = flops / sec / 1e12
@@ -311,7 +341,7 @@ def attention_sweep(dev, steps, warmup, workloads=None):
         out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L": w.Lq,
                     "window": w.window, "exps": exps,
                     "mask": "causal" if w.mask & 2 else "none", "us": round(sec * 1e6, 2),
-                    "host_us": round(host["s_per_step"] * 1e6, 2),
+                    "host_us": round(host["s_per_step"] * 1e6, 2), "calls": host["calls"],
                     "tflops": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)})
         log(f"  sweep {w.name}: {sec * 1e6:.1f} us, {tf:.1f} TFLOP/s "
             f"({100 * tf * 1e12 / PEAK_BF16_FLOPS:.1f}% of bf16 peak)")
@@ -370,14 +400,14 @@ def decode_sweep(dev, steps, warmup, copy_gbps=None):
         fn = lambda s: mha.mha_decode(s["q"], s["k"], s["v"], s["kv_lens"], out=s["o"],
                                       workspace=ws)
         host = {}
-        sec = time_eager(fn, sets, max(steps // 4, 2 * n_sets), max(warmup, n_sets), host)
+        sec = time_median(fn, sets, max(warmup, n_sets), host, min_calls=max(steps // 4, 2 * n_sets))
         lens = inp["kv_lens"]
         nbytes = accounting.attention_bytes(w.B, w.h, 1, w.Lk, w.d, w.mask, lens, w.dtype)
         flops = accounting.attention_flops(w.B, w.h, 1, w.Lk, w.d, w.mask, lens)
         gbps = nbytes / sec / 1e9
         out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L_cache": w.Lk,
                     "us": round(sec * 1e6, 2), "host_us": round(host["s_per_step"] * 1e6, 2),
-                    "gbps": round(gbps, 1),
+                    "calls": host["calls"], "gbps": round(gbps, 1),
                     "frac_peak_hbm": round(gbps * 1e9 / PEAK_HBM_BYTES, 4),
                     "frac_of_copy": round(gbps / copy_gbps, 4) if copy_gbps else None,
                     "tflops": round(flops / sec / 1e12, 2)})
@@ -444,16 +474,24 @@ def kernel_only_attention(w, dev, args):
             raise SystemExit("--kernel-only decode needs a decode workload")
         ws = torch.empty(int(mha.lib().mha_decode_workspace_bytes(w.B, w.h, w.Lk, w.d)),
                          dtype=torch.uint8, device=dev)
-        for _ in range(args.steps):
-            mha.mha_decode(inp["q"], inp["k"], inp["v"], inp["kv_lens"], out=o, workspace=ws)
+        call = lambda: mha.mha_decode(inp["q"], inp["k"], inp["v"], inp["kv_lens"], out=o,
+                                      workspace=ws)
     elif args.kernel_only == "attention":
-        for _ in range(args.steps):
-            mha.mha_forward(inp["q"], inp["k"], inp["v"], mask=w.mask, kv_lens=inp["kv_lens"],
-                            out=o, window=w.window)
+        call = lambda: mha.mha_forward(inp["q"], inp["k"], inp["v"], mask=w.mask,
+                                       kv_lens=inp["kv_lens"], out=o, window=w.window)
     else:
         raise SystemExit("attention workloads run the attention (or decode) kernels only")
+    warm = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.warm_seconds:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        warm += 10
+    for _ in range(args.steps):
+        call()
     torch.cuda.synchronize()
-    log(f"{args.kernel_only} on {w.name}: {args.steps} launches")
+    log(f"{args.kernel_only} on {w.name}: {warm} warm-up launches, then {args.steps} launches")
 
 
 def main():
