@@ -31,8 +31,10 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").double().numpy()
 
 
-def check(gpu, ref, dtype: str, what: str = ""):
-    """Compare a GPU result with the fp64 oracle; return (max_abs, max_rel)."""
+def check(gpu, ref, dtype: str, what: str = "", f32_atol: float = F32_ATOL):
+    """Compare a GPU result with the fp64 oracle; return (max_abs, max_rel).
+    f32_atol replaces the fp32 bound where a test derives a wider one from
+    its inputs' magnitudes (and says so)."""
     g = to_np(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, (what, g.shape, r.shape)
@@ -41,7 +43,7 @@ def check(gpu, ref, dtype: str, what: str = ""):
     max_abs = float(err.max()) if err.size else 0.0
     max_rel = float((err / np.maximum(np.abs(r), 1e-6)).max()) if err.size else 0.0
     if dtype == "f32":
-        assert max_abs <= F32_ATOL, f"{what}: max abs err {max_abs:.3e} > {F32_ATOL}"
+        assert max_abs <= f32_atol, f"{what}: max abs err {max_abs:.3e} > {f32_atol:.3e}"
     else:
         bound = BF16_ATOL + BF16_RTOL * np.abs(r)
         bad = err > bound
