@@ -32,9 +32,12 @@ def decode(q, k, v, lens, dev, **kw):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-# h up to 8, 16 and 32 select 1, 2 and 4 heads per lane group.
+# h up to 8, 16 and 32 select 1, 2 and 4 heads per lane group; above 32,
+# further workgroups take the next 32 heads (a partial last group at 40 and
+# 70).
 @pytest.mark.parametrize("B,h,L", [(5, 3, 1), (4, 8, 300), (3, 2, 1000), (9, 8, 4097),
-                                   (2, 16, 257), (3, 24, 700), (4, 32, 2100)])
+                                   (2, 16, 257), (3, 24, 700), (4, 32, 2100),
+                                   (3, 40, 1500), (2, 64, 2100), (2, 70, 300)])
 def test_decode_against_oracle(B, h, L, d):
     dev = device()
     say(f"case decode d={d} B={B} h={h} L={L}")

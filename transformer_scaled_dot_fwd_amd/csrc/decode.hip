@@ -55,13 +55,16 @@ __device__ __forceinline__ void dec_merge(DecState<D>& a, float m2, float l2, co
     a.m = m;
 }
 
-// Partial states of (sequence b, chunk s) for every head t, into
-// part[((b H + t) S + s) (D + 2) ..]: acc[0 .. D-1], m, l.
+// Partial states of (sequence b, chunk s) for heads t0 .. t0 + 8 HPL - 1
+// (t0 = 8 HPL blockIdx.y), into part[((b H + t) S + s) (D + 2) ..]:
+// acc[0 .. D-1], m, l.
 //
 // A cached key's row holds all H heads contiguously (H * D * 2 bytes), so a
-// wave reads whole rows: lane group g (8 lanes) takes heads g, g + 8, ...
-// (HPL of them), lane sl of the group d elements E sl .. E sl + E - 1.  Wave
-// w streams keys k0 + w, k0 + w + 4, ... of the chunk, two rows ahead.
+// wave reads whole rows (or, past 8 HPL heads, a contiguous 8 HPL-head
+// slice of them): lane group g (8 lanes) takes heads t0 + g, t0 + g + 8,
+// ... (HPL of them), lane sl of the group d elements E sl .. E sl + E - 1.
+// Wave w streams keys k0 + w, k0 + w + DEC_WAVES, ... of the chunk, two
+// rows ahead.
 template <int D, int HPL>
 __global__ __launch_bounds__(64 * DEC_WAVES) void decode_partial_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -80,6 +83,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_partial_bf16(
     const int w = (int)blockIdx.x;
     const int s = w % n_split;
     const int b = w / n_split;
+    const int t0 = 8 * HPL * (int)blockIdx.y;
 
     const int len = min(max(lens[b], 0), L);
     const int k0 = s * DEC_CHUNK;
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_partial_bf16(
     float qv[HPL][E];
 #pragma unroll
     for (int u = 0; u < HPL; ++u) {
-        const int t = g + 8 * u;
+        const int t = t0 + g + 8 * u;
         const bf16* qp = q + ((size_t)b * H + min(t, H - 1)) * D + E * sl;
 #pragma unroll
         for (int c = 0; c < NL; ++c) {
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_partial_bf16(
         const bool in = r < n_rounds;
 #pragma unroll
         for (int u = 0; u < HPL; ++u) {
-            const int t = g + 8 * u;
+            const int t = t0 + g + 8 * u;
             const uint32_t off = in && t < H ? (uint32_t)(((size_t)j * rs + (size_t)t * D + E * sl) * 2)
                                              : OOB_OFFSET;
 #pragma unroll
@@ -189,9 +193,10 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_partial_bf16(
     if (wave == 0) {
 #pragma unroll
         for (int u = 0; u < HPL; ++u) {
-            const int t = g + 8 * u;
+            const int tl = g + 8 * u;  // the head's slot in this workgroup
+            const int t = t0 + tl;
             for (int ww = 1; ww < DEC_WAVES; ++ww)
-                dec_merge<D>(st[u], red[ww][t][D], red[ww][t][D + 1], &red[ww][t][E * sl]);
+                dec_merge<D>(st[u], red[ww][tl][D], red[ww][tl][D + 1], &red[ww][tl][E * sl]);
             if (t < H) {
                 float* out = part + (((size_t)b * H + t) * n_split + s) * (D + 2);
 #pragma unroll
@@ -262,13 +267,19 @@ __global__ __launch_bounds__(64) void decode_merge_bf16(const float* __restrict_
 // outputs.
 int n_splits(int L) { return L > DEC_CHUNK ? (L + DEC_CHUNK - 1) / DEC_CHUNK : 1; }
 
+// Heads per lane group: 8 groups cover 8 HPL heads per workgroup; above 32
+// heads, further workgroups (grid axis y) take the next 32.
+int heads_per_group(int H) { return H <= 8 ? 1 : (H <= 16 ? 2 : 4); }
+
 template <int D, int HPL>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     const int n_split = n_splits(a.L);
     const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
     float* part = (float*)a.workspace;
-    hipLaunchKernelGGL((decode_partial_bf16<D, HPL>), dim3((unsigned)((long)a.B * n_split)),
-                       dim3(64 * DEC_WAVES), 0, stream, (const bf16*)a.q, (const bf16*)a.k,
+    const unsigned head_groups = (unsigned)((a.H + 8 * HPL - 1) / (8 * HPL));
+    hipLaunchKernelGGL((decode_partial_bf16<D, HPL>),
+                       dim3((unsigned)((long)a.B * n_split), head_groups), dim3(64 * DEC_WAVES),
+                       0, stream, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, a.lens, part, a.H, a.L, n_split, sl2e);
     hipLaunchKernelGGL(decode_merge_bf16<D>, dim3((unsigned)((long)a.B * a.H)), dim3(64), 0,
                        stream, (const float*)part, (bf16*)a.o, n_split);
@@ -281,15 +292,17 @@ size_t decode_workspace_bytes(int B, int H, int L, int D) {
     return (size_t)B * H * n_splits(L) * (D + 2) * sizeof(float);
 }
 
-// Heads per lane group: 8 groups cover up to 8 heads per pass.
+long long decode_partial_workgroups(int B, int L) { return (long long)B * n_splits(L); }
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+    const int hpl = heads_per_group(a.H);
     if (a.D == 128) {
-        if (a.H <= 8) return launch_decode_d<128, 1>(a, stream);
-        if (a.H <= 16) return launch_decode_d<128, 2>(a, stream);
+        if (hpl == 1) return launch_decode_d<128, 1>(a, stream);
+        if (hpl == 2) return launch_decode_d<128, 2>(a, stream);
         return launch_decode_d<128, 4>(a, stream);
     }
-    if (a.H <= 8) return launch_decode_d<64, 1>(a, stream);
-    if (a.H <= 16) return launch_decode_d<64, 2>(a, stream);
+    if (hpl == 1) return launch_decode_d<64, 1>(a, stream);
+    if (hpl == 2) return launch_decode_d<64, 2>(a, stream);
     return launch_decode_d<64, 4>(a, stream);
 }
 

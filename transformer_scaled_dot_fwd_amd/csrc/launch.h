@@ -49,6 +49,9 @@ struct DecodeArgs {
     void* workspace;
 };
 size_t decode_workspace_bytes(int B, int H, int L, int D);
+// Workgroups along the first grid axis of the partial-state kernel
+// (sequences x chunks of the cache); the host keeps it within INT_MAX.
+long long decode_partial_workgroups(int B, int L);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
 // The attention sub-layer's output with its residual and post-norm:
