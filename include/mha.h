@@ -50,7 +50,15 @@ typedef enum {
     MHA_ERR_LAUNCH = 3       /* the kernel launch failed */
 } mha_status;
 
-typedef enum { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype;
+/* The two sentinels give the enum the range of int, so any int a caller
+ * passes is a value of the type (an unknown code is rejected with
+ * MHA_ERR_INVALID_ARG, not undefined behaviour); they are not dtypes. */
+typedef enum {
+    MHA_F32 = 0,
+    MHA_BF16 = 1,
+    MHA_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    MHA_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
+} mha_dtype;
 
 /* Mask bit flags for M; MHA_MASK_KEY_PADDING | MHA_MASK_CAUSAL is their
  * union (-inf wherever either applies). */
@@ -260,8 +268,9 @@ int mha_self_attention_fused(mha_dtype dt, int B, int L, int d_model, int h, int
  *               scratch, nothing needs clearing); workspace_bytes its size.
  *               Calls that share a workspace must not run at the same time.
  *
- * Supported: MHA_BF16, d_k == d_v in {64, 128}, L_cache*h*d_k*2 < 2^31
- * (B == 0 is a no-op); MHA_ERR_UNSUPPORTED otherwise.  A workspace that is
+ * Supported: MHA_BF16, d_k == d_v in {64, 128}, any h >= 1 (heads are
+ * taken 32 at a time per workgroup), L_cache*h*d_k*2 < 2^31 (B == 0 is a
+ * no-op); MHA_ERR_UNSUPPORTED otherwise.  A workspace that is
  * NULL, misaligned or too small is MHA_ERR_INVALID_ARG.
  */
 size_t mha_decode_workspace_bytes(int B, int h, int L_cache, int d_k);

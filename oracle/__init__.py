@@ -231,10 +231,39 @@ class Oracle:
 _default = None
 
 
+def build_checked(out: str, verbose: bool = False) -> str:
+    """oracle.c built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (gcc), for a run of the pins under the sanitizers; load it into a
+    process that preloads gcc's libasan (``checked_runtime()``)."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-o", tmp, SOURCE, "-lm", "-Wall", "-Wextra"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def checked_runtime() -> str:
+    """gcc's shared ASan runtime (to preload before a checked build)."""
+    out = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True,
+                         text=True, check=True).stdout.strip()
+    if not os.path.isabs(out):
+        raise RuntimeError("gcc's libasan.so not found")
+    return out
+
+
 def default() -> Oracle:
-    """The oracle built from oracle.c (rebuilt when the source is newer)."""
+    """The oracle built from oracle.c (rebuilt when the source is newer);
+    ORACLE_CHECKED_LIBRARY names a sanitizer build to load instead."""
     global _default
     if _default is None:
+        checked = os.environ.get("ORACLE_CHECKED_LIBRARY")
+        if checked:
+            _default = Oracle(checked)
+            return _default
         if not os.path.exists(LIBRARY) or os.path.getmtime(SOURCE) > os.path.getmtime(LIBRARY):
             build()
         _default = Oracle(LIBRARY)

@@ -23,8 +23,15 @@ def declared_functions():
     return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mha_\w+)\s*\(", text, flags=re.M)
 
 
+# The sanitizer leg (tests/test_sanitized_host.py) reruns this module on a
+# host-only ASan/UBSan build of the same sources, named by this variable.
+CHECKED = os.environ.get("MHA_HOST_CHECKED_LIBRARY")
+
+
 @pytest.fixture(scope="module")
 def L():
+    if CHECKED:
+        return mha.declare(ctypes.CDLL(CHECKED))
     if not os.path.exists(mha.LIBRARY):
         from transformer_scaled_dot_fwd_amd import build
         build.build()
@@ -127,6 +134,7 @@ def test_fused_validation(L):
     assert call(B=0) == OK
 
 
+@pytest.mark.skipif(bool(CHECKED), reason="binding test; the checked library is loaded apart")
 def test_python_binding_checks_before_calling():
     import torch
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)

@@ -53,7 +53,14 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIBRARY} is not built; run `python -m transformer_scaled_dot_fwd_amd.build` "
             "(or __graft_entry__.build())")
-    L = ctypes.CDLL(LIBRARY)
+    _lib = declare(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the argument and return types of the C ABI on a loaded copy
+    of the library (the in-tree libmha.so, or a host-only checking build of
+    the same sources)."""
     i, p = ctypes.c_int, ctypes.c_void_p
     L.mha_forward.argtypes = [i, i, i, i, i, i, i, p, p, p, i, p, p, p]
     L.mha_forward.restype = i
@@ -74,7 +81,6 @@ def lib() -> ctypes.CDLL:
     L.mha_self_attention_fused.restype = i
     L.mha_status_string.argtypes = [i]
     L.mha_status_string.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

@@ -57,5 +57,40 @@ def build(verbose: bool = False) -> str:
     return LIBRARY
 
 
+def build_host_checked(out_dir: str, verbose: bool = False) -> str:
+    """A copy of the library whose host code is built with AddressSanitizer
+    and UndefinedBehaviorSanitizer (the device code is compiled as usual,
+    without them): the C ABI's argument validation can run under the
+    sanitizers on a machine without a GPU.  Load it into a process that
+    preloads the compiler's shared ASan runtime (``asan_runtime()``)."""
+    os.makedirs(out_dir, exist_ok=True)
+    host = [*COMMON, "-Xarch_host", "-O1", "-Xarch_host", "-g",
+            "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(out_dir, src.replace(".hip", ".host.o"))
+        objs.append(obj)
+        cmds.append([HIPCC, *host, "-c", os.path.join(CSRC, src), "-o", obj])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    out = os.path.join(out_dir, "libmha_host_checked.so")
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-shared-libsan",
+          "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+          "-o", out, *objs], verbose)
+    return out
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (to preload)."""
+    proc = subprocess.run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"],
+                          capture_output=True, text=True, check=True)
+    path = proc.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"ASan runtime not found ({path!r})")
+    return path
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -194,7 +194,8 @@ int mha_decode(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v, const 
     // One sequence's cache rows are addressed with 32-bit byte offsets; one
     // workgroup per (sequence, chunk of the cache).
     if ((long long)L_cache * h * d_k * 2 >= (1LL << 31)) return MHA_ERR_UNSUPPORTED;
-    if ((long long)B * (L_cache / 64 + 1) > INT_MAX) return MHA_ERR_UNSUPPORTED;
+    if (mha::decode_partial_workgroups(B, L_cache) > INT_MAX || (long long)B * h > INT_MAX)
+        return MHA_ERR_UNSUPPORTED;
     mha::DecodeArgs a{B, h, L_cache, d_k, q, k_cache, v_cache, cache_lens, o, workspace};
     return launch_status(mha::launch_decode_bf16(a, stream));
 }
