@@ -1,39 +1,36 @@
 #!/usr/bin/env python3
 """Benchmark of the multi-head attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c3] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
 
-One step is one pass of the whole hot path over one batch of seeded synthetic
-input: the Q/K/V projection, the masked attention and the W^O projection
-(the base decoder block by default: X [64, 128, 512], h = 8, d_k = 64,
-causal + key padding).  Where the self-attention rows are at most 128
-tokens long, the projection and the attention run as one fused kernel (two
-launches per step; ``--unfused`` keeps three).  The steps cycle over enough
-copies of every buffer that the 256 MB Infinity Cache cannot serve a repeat;
-K steps are launched back to back on one stream, bracketed by
-torch.cuda.synchronize() and HIP events on that stream (the host issues a
-step's two launches in a fraction of its GPU time, so the GPU never waits
-for the host).  The same steps replayed from HIP graphs (one graph holding a
-pass over all the copies, and one graph per step) are timed beside it: on
-this ROCm version a graph's kernel nodes cost about a microsecond more each
-than direct launches on a busy stream.
+The headline figure is the metric's own: attention-forward TFLOP/s at the
+base model's head shape (h = 8, d_k = 64) with L >= 1024.  One step is one
+mha_forward launch on each of the six rows of that sweep (L = 1024, 2048,
+4096 with B = 24576 / L, no mask and causal, bf16, seeded N(0,1) inputs),
+each on its own buffer set from a rotation of at least 1 GiB per row so the
+256 MB Infinity Cache cannot serve a repeat.  K steps are launched back to
+back on one stream, bracketed by torch.cuda.synchronize() and HIP events on
+that stream; the value is the steps' algorithmic FLOPs (4 d per legal
+(query, key) pair) over that time.
 
-Printed: one JSON line with the throughput (algorithmic TFLOP/s of the
-block), the roofline of the dominant kernel (timed alone with HIP events, in
-the same rotation, as graphs of one launch per buffer set so the host's
-per-call cost cannot show), the sub-layer with its residual and post-norm
-(LayerNorm(x + MultiHead(x)), W^O fused with the normalisation: its own
-HBM roofline and the sub-layer step time), attention-only sweeps (L >= 1024
-at the base and big head shapes, other head sizes, restricted attention),
-the decoding step against a K/V cache, and the fp64 CPU oracle timed on the
-host as a reported baseline, and a plain device copy's bandwidth.  The
-sweeps are timed as direct launches (each entry records the host's issue
-time per launch beside the GPU time and the calls per timed region); they
-and the per-kernel figures report the median of five timed regions of at
-least 20 ms or 2 passes over the buffer sets.
+Printed beside it, in the same JSON line:
+* every row of the sweep timed alone (h = 8 and h = 16, and the long
+  causal workload), and the roofline of the dominant kernel: the streaming
+  attention kernel on the step's longest row, its average launch duration
+  timed with HIP events on the stream it runs on;
+* the short-sequence workloads, HBM-bound: base encoder self-attention
+  with key padding, big cross-attention over encoder memory, and the
+  attention of the base decoder block, as algorithmic GB/s against the
+  8 TB/s peak and against a measured device copy;
+* the base decoder block step (projection, attention, W^O; fused
+  projection + attention where rows are at most 128 tokens) with its
+  per-kernel figures and the sub-layer with its residual and post-norm;
+* the other head sizes, restricted attention and the decoding step;
+* the fp64 CPU oracle timed on the host: on a sample of the headline rows
+  (the reported baseline) and per configuration.
 
 Counter runs: ``--kernel-only NAME`` runs just one kernel (or a plain
-device copy of known size, ``copy``) so rocprofv3 --pmc can read its
+device copy of known size, ``copy``) so rocprofv3 can trace it or read its
 FETCH_SIZE / WRITE_SIZE.
 """
 from __future__ import annotations
@@ -85,7 +82,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--workload", default="c3",
+                    help="with --kernel-only: the workload the kernel runs on")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -301,50 +299,142 @@ def time_median(fn, sets, warmup, host=None, min_calls=0, min_sec=0.02, repeats=
 
 def traffic_for(name, launches_key):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None
-    when absent or taken on a different version of the kernel source."""
+    when absent or taken on a different version of the kernel source.
+    Entries are keyed "kernel@workload" (or, for the block's kernels,
+    by kernel name with the workload recorded inside)."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    e = t.get(name)
+    e = t.get(f"{name}@{launches_key}") or t.get(name)
     if not e or e.get("source_sha") != source_sha(name) or e.get("workload") != launches_key:
         return None
     return e.get("bytes_per_launch")
+
+
+def attention_sets(w, dev, n_max=16):
+    """Rotating device copies of an attention workload's inputs (each with
+    its own output), enough to cover ROTATE_BYTES."""
+    import torch
+    from workloads import configs
+    inp = configs.make_inputs(w)
+    one = working_set_bytes([inp["q"], inp["k"], inp["v"], inp["q"]])
+    n_sets = max(2, min(n_max, math.ceil(ROTATE_BYTES / one)))
+    sets = []
+    for _ in range(n_sets):
+        s = {k: v.to(dev) if v is not None else None for k, v in inp.items()}
+        s["o"] = torch.empty_like(s["q"])
+        sets.append(s)
+    return inp, sets
+
+
+def attention_call(w):
+    import transformer_scaled_dot_fwd_amd as mha
+    return lambda s: mha.mha_forward(s["q"], s["k"], s["v"], mask=w.mask, kv_lens=s["kv_lens"],
+                                     out=s["o"], window=w.window)
 
 
 def attention_sweep(dev, steps, warmup, workloads=None):
     """Attention alone at the base (h=8) and big (h=16) shapes, L >= 1024,
     plus the long causal workload (or the given workloads)."""
     import torch
-    import transformer_scaled_dot_fwd_amd as mha
     from workloads import accounting, configs
     out = []
     if workloads is None:
         workloads = [configs.get("c5")] + configs.sweep()
     for w in workloads:
-        inp = configs.make_inputs(w)
-        one = working_set_bytes([inp["q"], inp["k"], inp["v"], inp["q"]])
-        n_sets = max(2, min(16, math.ceil(ROTATE_BYTES / one)))
-        sets = []
-        for _ in range(n_sets):
-            s = {k: v.to(dev) if v is not None else None for k, v in inp.items()}
-            s["o"] = torch.empty_like(s["q"])
-            sets.append(s)
-        fn = lambda s: mha.mha_forward(s["q"], s["k"], s["v"], mask=w.mask,
-                                       kv_lens=s["kv_lens"], out=s["o"], window=w.window)
+        inp, sets = attention_sets(w, dev)
+        fn = attention_call(w)
         host = {}
-        sec = time_median(fn, sets, max(warmup, n_sets), host, min_calls=max(steps // 4, 2 * n_sets))
+        sec = time_median(fn, sets, max(warmup, len(sets)), host,
+                          min_calls=max(steps // 4, 2 * len(sets)))
         flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, inp["kv_lens"],
                                            w.window)
         tf = flops / sec / 1e12
         exps = accounting.legal_pairs(w.B, w.h, w.Lq, w.Lk, w.mask, inp["kv_lens"], w.window)
         out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L": w.Lq,
-                    "window": w.window, "exps": exps,
+                    "window": w.window, "exps": exps, "flops": flops,
                     "mask": "causal" if w.mask & 2 else "none", "us": round(sec * 1e6, 2),
                     "host_us": round(host["s_per_step"] * 1e6, 2), "calls": host["calls"],
                     "tflops": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)})
         log(f"  sweep {w.name}: {sec * 1e6:.1f} us, {tf:.1f} TFLOP/s "
             f"({100 * tf * 1e12 / PEAK_BF16_FLOPS:.1f}% of bf16 peak)")
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
+def metric_step(dev, steps, warmup):
+    """The headline step: one mha_forward launch per row of metric_rows()
+    (h = 8, d_k = 64, L >= 1024, no mask and causal), each row cycling over
+    its own rotating buffer sets.  Returns seconds per step, FLOPs per step
+    and the rows."""
+    import torch
+    from workloads import accounting, configs
+    rows = []
+    for w in configs.metric_rows():
+        inp, sets = attention_sets(w, dev, n_max=12)
+        rows.append({"w": w, "sets": sets, "fn": attention_call(w),
+                     "flops": accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask,
+                                                         inp["kv_lens"])})
+    counter = [0]
+
+    def step(_):
+        i = counter[0]
+        for r in rows:
+            r["fn"](r["sets"][i % len(r["sets"])])
+        counter[0] = i + 1
+
+    warm_gpu(step, [None], 0.3)
+    host = {}
+    sec = time_eager(step, [None], steps, warmup, host)
+    flops = sum(r["flops"] for r in rows)
+    desc = [f"{r['w'].name} ({len(r['sets'])} sets)" for r in rows]
+    del rows
+    torch.cuda.empty_cache()
+    return sec, flops, host["s_per_step"], desc
+
+
+def hbm_workloads(dev, steps, warmup, copy_gbps):
+    """The short-sequence workloads, whose attention is HBM-bound (FLOP per
+    byte far under the ridge point of 2.5e15 / 8e12 = 312): algorithmic
+    bytes (Q and O once, the legal K/V rows, the lengths) per second."""
+    import torch
+    import transformer_scaled_dot_fwd_amd as mha
+    from workloads import accounting, configs
+    out = []
+    for name in ("c2", "c4", "c3"):
+        w = configs.get(name)
+        if w.block:
+            # the block's attention on its own projected Q, K, V
+            inputs = configs.make_inputs(w)
+            probe = Block(w, inputs, dev, 1)
+            s0 = probe.sets[0]
+            one = working_set_bytes([s0[k] for k in ("q", "k", "v", "o")])
+            del probe
+            blk = Block(w, inputs, dev, max(2, min(16, math.ceil(ROTATE_BYTES / one))))
+            for s in blk.sets:
+                blk.project_qkv(s)
+            sets, fn, lens = blk.sets, blk.attention, inputs["kv_lens"]
+            what = "attention of the base decoder block (causal + key padding)"
+        else:
+            inp, sets = attention_sets(w, dev)
+            fn, lens = attention_call(w), inp["kv_lens"]
+            what = w.description
+        host = {}
+        sec = time_median(fn, sets, max(warmup, len(sets)), host,
+                          min_calls=max(steps // 4, 2 * len(sets)))
+        nbytes = accounting.attention_bytes(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, lens, w.dtype)
+        flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, lens)
+        gbps = nbytes / sec / 1e9
+        out.append({"workload": w.name, "what": what, "bound": "hbm", "bytes": nbytes,
+                    "us": round(sec * 1e6, 2), "host_us": round(host["s_per_step"] * 1e6, 2),
+                    "calls": host["calls"], "gbps": round(gbps, 1),
+                    "frac_peak_hbm": round(gbps * 1e9 / PEAK_HBM_BYTES, 4),
+                    "frac_of_copy": round(gbps / copy_gbps, 4) if copy_gbps else None,
+                    "tflops": round(flops / sec / 1e12, 1)})
+        log(f"  hbm {w.name}: {sec * 1e6:.2f} us, {gbps:.0f} GB/s "
+            f"({100 * gbps * 1e9 / PEAK_HBM_BYTES:.1f}% of HBM peak)")
         del sets
         torch.cuda.empty_cache()
     return out
@@ -428,37 +518,144 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, inputs, budget_s):
-    """The fp64 oracle (as it stands) on a bounded sample of the same
-    workload: the block over whole batch rows, repeated until about
-    budget_s seconds of host time have passed."""
+def sample_rows(w, n, seed):
+    """n random (b, head, i) rows of an attention workload."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.integers(0, w.B, n), rng.integers(0, w.h, n),
+                     rng.integers(0, w.Lq, n)], axis=1).astype(np.int64)
+
+
+def row_flops(w, rows, kv_lens):
+    """Algorithmic FLOPs of the given rows: 4 d per legal key."""
+    import numpy as np
+    b, i = rows[:, 0], rows[:, 2]
+    n = np.full(len(rows), w.Lk, dtype=np.int64)
+    if w.mask & 1:
+        n = np.minimum(n, np.clip(np.asarray(kv_lens, dtype=np.int64)[b], 0, w.Lk))
+    if w.mask & 2:
+        n = np.minimum(n, i + 1)
+    return int(4 * w.d * n.sum())
+
+
+def oracle_rows_rate(w, budget_s, seed):
+    """The oracle's attention over random rows of workload w, doubling the
+    sample until it takes about budget_s: (seconds, rows, FLOPs)."""
     import oracle
-    from workloads import accounting
-    x, ws = inputs["x"], [inputs[k] for k in ("w_q", "w_k", "w_v", "w_o")]
-    lens = inputs["kv_lens"]
-
-    def run(nb):
+    from workloads import configs
+    inp = configs.make_inputs(w)
+    n = 64
+    while True:
+        rows = sample_rows(w, n, seed)
         t0 = time.perf_counter()
-        oracle.mha_block(x[:nb], x[:nb], *ws, h=w.h, mask=w.mask,
-                         kv_lens=None if lens is None else lens[:nb])
-        return time.perf_counter() - t0
+        oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, mask=w.mask,
+                              kv_lens=inp["kv_lens"], window=w.window)
+        sec = time.perf_counter() - t0
+        if sec >= budget_s / 2 or n >= 1 << 20:
+            return sec, n, row_flops(w, rows, inp["kv_lens"])
+        n *= 2
 
-    def flops(nb):
-        sub = accounting.workload_work(dataclasses.replace(w, B=nb),
-                                       None if lens is None else lens[:nb].numpy())
-        return sub["total_flops"]
 
-    probe = run(1)
-    nb = int(max(1, min(w.B, budget_s / max(probe, 1e-3))))
-    total_s, total_f, reps = 0.0, 0, 0
-    while total_s < budget_s or reps == 0:
-        total_s += run(nb)
-        total_f += flops(nb)
-        reps += 1
+def cpu_baseline(budget_s):
+    """The fp64 oracle (as it stands) on a bounded sample of the headline
+    workload: random rows of each of the six rows of metric_rows(), about
+    budget_s seconds in all."""
+    import oracle
+    from workloads import configs
+    total_s, total_f, parts = 0.0, 0, []
+    rows = configs.metric_rows()
+    for n, w in enumerate(rows):
+        sec, nr, f = oracle_rows_rate(w, budget_s / len(rows), 31 + n)
+        total_s += sec
+        total_f += f
+        parts.append(f"{nr} rows of {w.name}")
     return {"value": round(total_f / total_s / 1e12, 6), "unit": "TFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": f"the block (projection, attention, W^O) over {nb} of {w.B} batch rows, "
-                      f"{reps} runs, {total_s:.1f} s"}
+            "sample": "random query rows (all heads, both masks) of the h=8 d_k=64 L>=1024 "
+                      f"rows: {', '.join(parts)}; {total_s:.1f} s of oracle time, "
+                      f"{total_f / 1e9:.2f} GFLOP"}
+
+
+def oracle_per_config(budget_s):
+    """The oracle's seconds for each configuration: c1 (best of 100), c2,
+    c3 (the whole block) and c4 (best of 3) in full; c5 and the headline
+    rows extrapolated from a timed sample of random rows by FLOPs (stated
+    per entry)."""
+    import oracle
+    from workloads import accounting, configs
+    out = {}
+
+    def best(fn, n):
+        t = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - t0)
+        return min(t)
+
+    for name, reps in (("c1", 100), ("c2", 3), ("c3", 1), ("c4", 1)):
+        w = configs.get(name)
+        inp = configs.make_inputs(w)
+        lens = inp["kv_lens"]
+        if w.block:
+            fn = lambda: oracle.mha_block(inp["x"], inp["x"], inp["w_q"], inp["w_k"],
+                                          inp["w_v"], inp["w_o"], h=w.h, mask=w.mask,
+                                          kv_lens=lens)
+            flops = accounting.workload_work(w, lens.numpy())["total_flops"]
+        else:
+            fn = lambda: oracle.attention(inp["q"], inp["k"], inp["v"], mask=w.mask,
+                                          kv_lens=lens)
+            flops = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, lens)
+        sec = best(fn, reps)
+        out[name] = {"workload": w.name, "seconds": round(sec, 4),
+                     "gflops": round(flops / sec / 1e9, 3), "how": f"full, best of {reps}"}
+    for w in [configs.get("c5")] + configs.metric_rows():
+        sec, nr, f = oracle_rows_rate(w, budget_s / 7, 77)
+        # these workloads have no key padding: no lengths
+        full = accounting.attention_flops(w.B, w.h, w.Lq, w.Lk, w.d, w.mask)
+        rate = f / sec
+        key = "c5" if w.name == configs.get("c5").name else w.name
+        out[key] = {"workload": w.name, "seconds": round(full / rate, 2),
+                    "gflops": round(rate / 1e9, 3),
+                    "how": f"extrapolated by FLOPs from {nr} random rows ({sec:.2f} s)"}
+    return out
+
+
+def kernel_only_block(w, dev, args):
+    """One kernel of the block workload alone (or a device copy), for trace
+    and counter runs."""
+    import torch
+    inputs = configs_make(w)
+    blk = Block(w, inputs, dev, 4)
+    for s in blk.sets:
+        blk.project_qkv(s)
+    if args.kernel_only == "copy":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy: 256 MiB per launch")
+        return
+    if args.kernel_only == "decode":
+        raise SystemExit("--kernel-only decode needs a decode workload")
+    fn = getattr(blk, args.kernel_only)
+    t0 = time.perf_counter()
+    warm = 0
+    while time.perf_counter() - t0 < args.warm_seconds:
+        fn(blk.sets[warm % len(blk.sets)])
+        warm += 1
+        if warm % 50 == 0:
+            torch.cuda.synchronize()
+    for i in range(args.steps):
+        fn(blk.sets[i % len(blk.sets)])
+    torch.cuda.synchronize()
+    log(f"{args.kernel_only} on {w.name}: {warm} warm-up launches, then {args.steps} launches")
+
+
+def configs_make(w):
+    from workloads import configs
+    return configs.make_inputs(w)
 
 
 def kernel_only_attention(w, dev, args):
@@ -494,6 +691,87 @@ def kernel_only_attention(w, dev, args):
     log(f"{args.kernel_only} on {w.name}: {warm} warm-up launches, then {args.steps} launches")
 
 
+def block_step(dev, args, copy_gbps):
+    """The base decoder block (c3): the step, every kernel of it timed alone
+    in the same rotation, the dominant kernel's roofline, and the sub-layer
+    with its residual and post-norm."""
+    import torch
+    from workloads import accounting, configs
+    w = configs.get("c3")
+    inputs = configs.make_inputs(w)
+    work = accounting.workload_work(w, inputs["kv_lens"].numpy())
+    probe = Block(w, inputs, dev, 1)
+    s0 = probe.sets[0]
+    one = working_set_bytes([s0[k] for k in ("x", "w_q", "w_k", "w_v", "w_o", "q", "k", "v",
+                                             "o", "y", "z")])
+    n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / one)))
+    del probe
+    blk = Block(w, inputs, dev, n_sets)
+    blk.fused = (not args.unfused) and blk.fused_supported()
+    log(f"block {w.name}: working set {one / 1e6:.1f} MB x {n_sets} rotating sets; "
+        f"{'fused self-attention + W^O' if blk.fused else 'projection + attention + W^O'}")
+    warm_gpu(blk.step, blk.sets, 0.3)
+    host = {}
+    sec_step = time_eager(blk.step, blk.sets, args.steps, args.warmup, host)
+    sec_graph = time_steps(blk.step, blk.sets, args.steps, args.warmup)
+    sec_warm = time_eager(blk.step, blk.sets[:1], args.steps, args.warmup)
+    flops_step = work["total_flops"]
+    log(f"block step: {sec_step * 1e6:.2f} us, {flops_step / sec_step / 1e12:.1f} TFLOP/s")
+
+    step_kernels = (["self_attention_fused", "out_proj"] if blk.fused
+                    else ["project_qkv", "attention", "out_proj"])
+    names = step_kernels + (["project_qkv", "attention"] if blk.fused else [])
+    names.append("out_proj_post_norm")
+    per = {}
+    for name in names:
+        per[name] = kernel_time(getattr(blk, name), blk.sets, max(args.steps, 2 * n_sets),
+                                args.warmup)
+        log(f"  {name}: {per[name] * 1e6:.2f} us"
+            + ("" if name in step_kernels else " (not in the step)"))
+    dom = max(step_kernels, key=per.get)
+    if dom == "attention":
+        bound, alg, unit, peak = "hbm", work["attention"]["bytes"], "GB/s", PEAK_HBM_BYTES
+    else:
+        bound, alg, unit, peak = "mfma", work[dom]["flops"], "TFLOP/s", PEAK_BF16_FLOPS
+    scale = 1e9 if unit == "GB/s" else 1e12
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(alg / per[dom] / scale, 2),
+                "peak": round(peak / scale, 1), "unit": unit,
+                "frac": round(alg / per[dom] / peak, 4), "traffic": traffic_for(dom, w.name),
+                "avg_launch_us": round(per[dom] * 1e6, 3)}
+    kernels = {name: {"us": round(sec * 1e6, 3),
+                      "tflops": round(work[name]["flops"] / sec / 1e12, 1),
+                      "gbps": round(work[name]["bytes"] / sec / 1e9, 1),
+                      "in_step": name in step_kernels} for name, sec in per.items()}
+    pn = "out_proj_post_norm"
+    pn_bytes = work[pn]["bytes"]
+    sec_sub = time_eager(blk.sublayer_step, blk.sets, args.steps, args.warmup)
+    post_norm = {
+        "kernel": pn, "bound": "hbm", "us": round(per[pn] * 1e6, 3),
+        "achieved": round(pn_bytes / per[pn] / 1e9, 1), "peak": PEAK_HBM_BYTES / 1e9,
+        "unit": "GB/s", "frac": round(pn_bytes / per[pn] / PEAK_HBM_BYTES, 4),
+        "frac_of_copy": round(pn_bytes / per[pn] / 1e9 / copy_gbps, 4),
+        "tflops": round(work[pn]["flops"] / per[pn] / 1e12, 1),
+        "intensity_flop_per_byte": round(work[pn]["flops"] / pn_bytes, 1),
+        "traffic": traffic_for(pn, w.name),
+        "vs_out_proj_gemm_us": round(per["out_proj"] * 1e6, 3),
+        "sublayer_step_us": round(sec_sub * 1e6, 3),
+        "sublayer_step": " -> ".join(step_kernels[:-1] + [pn]),
+    }
+    out = {"workload": w.name, "description": w.description,
+           "step": " -> ".join(step_kernels) + f" (direct launches over {n_sets} buffer sets)",
+           "us_per_step": round(sec_step * 1e6, 3),
+           "us_per_step_host_issue": round(host["s_per_step"] * 1e6, 3),
+           "us_per_step_graphs": round(sec_graph * 1e6, 3),
+           "us_per_step_warm_cache": round(sec_warm * 1e6, 3),
+           "flops_per_step": flops_step,
+           "tflops": round(flops_step / sec_step / 1e12, 2),
+           "frac_peak_bf16": round(flops_step / sec_step / PEAK_BF16_FLOPS, 4),
+           "kernels": kernels, "roofline": roofline, "post_norm": post_norm}
+    del blk
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -509,127 +787,47 @@ def main():
     mha.lib()  # fail loudly if the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = configs.get(args.workload)
-    if args.kernel_only and not w.block:
-        return kernel_only_attention(w, dev, args)
-    if not w.block:
-        raise SystemExit("the benchmark step is the full block: pick a block workload (c3)")
-    inputs = configs.make_inputs(w)
-    work = accounting.workload_work(w, inputs["kv_lens"].numpy()
-                                    if inputs["kv_lens"] is not None else None)
-
-    probe = Block(w, inputs, dev, 1)
-    s0 = probe.sets[0]
-    one = working_set_bytes([s0[k] for k in ("x", "w_q", "w_k", "w_v", "w_o", "q", "k", "v",
-                                             "o", "y", "z")])
-    n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / one)))
-    del probe
-    blk = Block(w, inputs, dev, n_sets)
-    blk.fused = (not args.unfused) and blk.fused_supported()
-    log(f"workload {w.name}: working set {one / 1e6:.1f} MB x {n_sets} rotating sets; "
-        f"{'fused self-attention + W^O' if blk.fused else 'projection + attention + W^O'}")
 
     if args.kernel_only:
-        fns = {"project_qkv": blk.project_qkv, "attention": blk.attention,
-               "out_proj": blk.out_proj, "self_attention_fused": blk.self_attention_fused,
-               "out_proj_post_norm": blk.out_proj_post_norm}
-        if args.kernel_only == "copy":
-            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-            dst = torch.empty_like(src)
-            for _ in range(args.steps):
-                dst.copy_(src)
-            torch.cuda.synchronize()
-            log("copy: 256 MiB per launch")
-        else:
-            for i in range(args.steps):
-                fns[args.kernel_only](blk.sets[i % n_sets])
-            torch.cuda.synchronize()
-            log(f"{args.kernel_only}: {args.steps} launches")
-        return
+        w = configs.get(args.workload)
+        if not w.block:
+            return kernel_only_attention(w, dev, args)
+        return kernel_only_block(w, dev, args)
 
-    # ---- whole step: K steps, each on its own buffer set, as graph replays ----
-    warm_gpu(blk.step, blk.sets, 0.3)
-    host = {}
-    sec_step = time_eager(blk.step, blk.sets, args.steps, args.warmup, host)
-    log(f"host time to issue one step's launches: {host['s_per_step'] * 1e6:.2f} us")
-    sec_step_graph = time_steps(blk.step, blk.sets, args.steps, args.warmup)
-    log(f"graphs of {len(blk.sets)} steps: {sec_step_graph * 1e6:.2f} us")
-    sec_step_1g = time_graphs(capture(blk.step, blk.sets), args.steps, args.warmup)
-    log(f"one graph per step: {sec_step_1g * 1e6:.2f} us")
-    # labelled warm-cache figure: every step on the same buffer set, so the
-    # inputs stay in the 256 MB Infinity Cache (not the reported value)
-    sec_step_warm = time_eager(blk.step, blk.sets[:1], args.steps, args.warmup)
-    log(f"warm cache (one buffer set): {sec_step_warm * 1e6:.2f} us")
-    flops_step = work["total_flops"]
+    # ---- the headline step: the h = 8 rows of the L >= 1024 sweep ----
+    sec_step, flops_step, host_s, desc = metric_step(dev, args.steps, args.warmup)
     value = flops_step / sec_step / 1e12
-    log(f"step: {sec_step * 1e6:.2f} us, {value:.1f} TFLOP/s")
+    log(f"step (h=8 L>=1024 rows): {sec_step * 1e6:.1f} us, {value:.1f} TFLOP/s "
+        f"({100 * value * 1e12 / PEAK_BF16_FLOPS:.1f}% of bf16 peak)")
 
-    # ---- per-kernel durations, each timed alone in the same rotation: the
-    # kernels of the step, then (for reference) those of the other path ----
-    step_kernels = (["self_attention_fused", "out_proj"] if blk.fused
-                    else ["project_qkv", "attention", "out_proj"])
-    names = step_kernels + (["project_qkv", "attention"] if blk.fused else [])
-    names.append("out_proj_post_norm")
-    per = {}
-    for name in names:
-        fn = getattr(blk, name)
-        per[name] = kernel_time(fn, blk.sets, max(args.steps, 2 * n_sets), args.warmup)
-        log(f"  {name}: {per[name] * 1e6:.2f} us"
-            + ("" if name in step_kernels else " (not in the step)"))
-    dom = max(step_kernels, key=per.get)
-    if dom == "attention":
-        bound, alg, unit, peak = "hbm", work["attention"]["bytes"], "GB/s", PEAK_HBM_BYTES
-    else:
-        bound, alg, unit, peak = "mfma", work[dom]["flops"], "TFLOP/s", PEAK_BF16_FLOPS
-    achieved = alg / per[dom]
-    scale = 1e9 if unit == "GB/s" else 1e12
-    traffic = traffic_for(dom, w.name)
-    roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved / scale, 2),
-                "peak": round(peak / scale, 1), "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic,
-                "avg_launch_us": round(per[dom] * 1e6, 3)}
-    kernels = {}
-    for name, sec in per.items():
-        f = work[name]["flops"]
-        b = work[name]["bytes"]
-        kernels[name] = {"us": round(sec * 1e6, 3), "tflops": round(f / sec / 1e12, 1),
-                         "gbps": round(b / sec / 1e9, 1), "in_step": name in step_kernels}
-
-    # ---- the sub-layer with its residual and post-norm (W^O, + x, LayerNorm
-    # in one kernel), an HBM-bound kernel: arithmetic intensity under the
-    # ridge point of 2.5e15 / 8e12 = 312 FLOP/B ----
-    pn = "out_proj_post_norm"
-    pn_bytes = work[pn]["bytes"]
-    sec_sub = time_eager(blk.sublayer_step, blk.sets, args.steps, args.warmup)
-    post_norm = {
-        "kernel": pn, "bound": "hbm", "us": round(per[pn] * 1e6, 3),
-        "achieved": round(pn_bytes / per[pn] / 1e9, 1), "peak": PEAK_HBM_BYTES / 1e9,
-        "unit": "GB/s", "frac": round(pn_bytes / per[pn] / PEAK_HBM_BYTES, 4),
-        "tflops": round(work[pn]["flops"] / per[pn] / 1e12, 1),
-        "intensity_flop_per_byte": round(work[pn]["flops"] / pn_bytes, 1),
-        "traffic": traffic_for(pn, w.name),
-        "vs_out_proj_gemm_us": round(per["out_proj"] * 1e6, 3),
-        "sublayer_step_us": round(sec_sub * 1e6, 3),
-        "sublayer_step": " -> ".join(step_kernels[:-1] + [pn]),
-    }
-    log(f"  sub-layer with post-norm: {sec_sub * 1e6:.2f} us per step; {pn} "
-        f"{per[pn] * 1e6:.2f} us, {post_norm['achieved']:.0f} GB/s")
-
-    sweep = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup)
-    heads = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup,
-                                                       configs.head_sizes())
-    windowed = None if args.no_sweep else attention_sweep(dev, args.steps, args.warmup,
-                                                          configs.windows())
+    # ---- every sweep row alone; the dominant kernel's roofline ----
+    sweep = attention_sweep(dev, args.steps, args.warmup)
+    rows8 = {r.name for r in configs.metric_rows()}
+    dom = max((e for e in sweep if e["workload"] in rows8), key=lambda e: e["us"])
+    roofline = {"kernel": "attn_fwd_bf16 (streaming attention, d=64)",
+                "workload": dom["workload"], "bound": "mfma",
+                "achieved": round(dom["flops"] / (dom["us"] * 1e-6) / 1e12, 1),
+                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": dom["frac_peak_bf16"],
+                "traffic": traffic_for("attention", dom["workload"]),
+                "avg_launch_us": dom["us"],
+                "algorithmic_flops_per_launch": dom["flops"]}
     copy = copy_bandwidth(dev)
     log(f"device copy: {copy['gbps']:.0f} GB/s read + written "
         f"({100 * copy['frac_peak_hbm']:.1f}% of the HBM peak)")
-    post_norm["frac_of_copy"] = round(post_norm["achieved"] / copy["gbps"], 4)
-    decoded = None if args.no_sweep else decode_sweep(dev, args.steps, args.warmup,
-                                                      copy["gbps"])
-    cpu = None
+    hbm = hbm_workloads(dev, args.steps, args.warmup, copy["gbps"])
+    block = block_step(dev, args, copy["gbps"])
+    heads = windowed = decoded = None
+    if not args.no_sweep:
+        heads = attention_sweep(dev, args.steps, args.warmup, configs.head_sizes())
+        windowed = attention_sweep(dev, args.steps, args.warmup, configs.windows())
+        decoded = decode_sweep(dev, args.steps, args.warmup, copy["gbps"])
+    cpu = oracle_cfg = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inputs, args.cpu_seconds)
+        cpu = cpu_baseline(args.cpu_seconds)
         log(f"cpu baseline: {cpu}")
+        oracle_cfg = oracle_per_config(args.cpu_seconds)
+        log(f"oracle per config: {oracle_cfg}")
 
     line = {
         "metric": "attention fwd TFLOP/s & % peak bf16 MFMA at h=8,d_k=64 (1 MI355X)",
@@ -639,31 +837,28 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(sec_step * 1e3, 5),
-        "ms_per_step_host_issue": round(host["s_per_step"] * 1e3, 5),
-        "ms_per_step_graphs": round(sec_step_graph * 1e3, 5),
-        "ms_per_step_one_graph_per_step": round(sec_step_1g * 1e3, 5),
-        "ms_per_step_warm_cache": round(sec_step_warm * 1e3, 5),
+        "ms_per_step_host_issue": round(host_s * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) inputs, N(0,1/512) weights, lengths U{32..128})",
-        "config": {"workload": w.name, "B": w.B, "L": w.Lq, "d_model": w.d_model, "h": w.h,
-                   "d_k": w.d, "mask": "causal+key_padding",
-                   "step": " -> ".join(step_kernels)
-                   + f" (direct launches on one stream over {len(blk.sets)} buffer sets)",
-                   "rotating_sets": n_sets,
-                   "flops_per_step": flops_step},
+        "data": "synthetic (seeded i.i.d. N(0,1) Q/K/V, bf16)",
+        "config": {"workload": "attention forward, h=8 d_k=64, L in {1024, 2048, 4096} with "
+                               "B = 24576/L, no mask and causal (six mha_forward launches "
+                               "per step)",
+                   "rows": desc, "h": 8, "d_k": 64, "flops_per_step": flops_step,
+                   "value_is": "sum of the six rows' algorithmic FLOPs / step time"},
         "frac_peak_bf16": round(value * 1e12 / PEAK_BF16_FLOPS, 4),
-        "kernels": kernels,
         "roofline": roofline,
-        "hbm_copy": copy,
-        "post_norm": post_norm,
         "attention_sweep": sweep,
+        "hbm_workloads": hbm,
+        "hbm_copy": copy,
+        "block_step": block,
         "head_size_sweep": heads,
         "window_sweep": windowed,
         "decode_sweep": decoded,
         "cpu_baseline": cpu,
+        "oracle_per_config": oracle_cfg,
     }
     print(json.dumps(line), flush=True)
 

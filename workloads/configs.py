@@ -93,6 +93,12 @@ def sweep():
     return out
 
 
+def metric_rows():
+    """The rows the headline figure aggregates: the L >= 1024 sweep at the
+    base model's head shape (h = 8, d_k = 64), no mask and causal."""
+    return [w for w in sweep() if w.h == 8]
+
+
 def head_sizes():
     """The other head shapes of the base model's width (d_model 512; Deep-
     reading page section 08, Table 3, rows (A)): h=32 d=16, h=16 d=32, h=4
