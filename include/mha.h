@@ -47,7 +47,9 @@ typedef enum {
                                 CAUSAL with Lq != Lk, an unknown dtype/mask */
     MHA_ERR_UNSUPPORTED = 2, /* valid but not compiled: d_k != d_v, a head
                                 size or GEMM width outside the built set */
-    MHA_ERR_LAUNCH = 3       /* the kernel launch failed */
+    MHA_ERR_LAUNCH = 3,      /* the kernel launch failed */
+    MHA_ERR_SCRATCH = 4      /* mha_decode_noalloc: the call needs more than
+                                MHA_DECODE_SCRATCH_BYTES of partial states */
 } mha_status;
 
 /* The two sentinels give the enum the range of int, so any int a caller
@@ -278,6 +280,31 @@ int mha_decode(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v,
                const void* q, const void* k_cache, const void* v_cache,
                const int32_t* cache_lens, void* o,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mha_decode_noalloc -- mha_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same kernels and result (bit for bit) as mha_decode,
+ * with the partial states in a static scratch buffer of the library instead
+ * of a caller workspace; the call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine).
+ *
+ * Limit: mha_decode_workspace_bytes(B, h, L_cache, d_k) must not exceed
+ * MHA_DECODE_SCRATCH_BYTES (16 MiB: e.g. 64 sequences x 16 heads with caches
+ * of up to 32768 positions at d_k = 64, which need 8.7 MB); larger calls
+ * return MHA_ERR_SCRATCH and launch nothing.  Each GPU the library runs on holds its own copy of the
+ * buffer until the process ends, looked up on the first call on that GPU.
+ * Every call on one GPU shares that copy, so calls that overlap in time on
+ * one GPU (on different streams, or from different host threads) race and
+ * must be ordered by the caller; calls on one stream are ordered already.
+ * Nothing in the buffer needs clearing between calls.
+ *
+ * Arguments, other status codes and support: as mha_decode.
+ */
+#define MHA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+int mha_decode_noalloc(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v,
+                       const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cache_lens, void* o, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* mha_status_string(int status);

@@ -12,7 +12,7 @@ import pytest
 
 import transformer_scaled_dot_fwd_amd as mha
 
-OK, INVALID, UNSUPPORTED, LAUNCH = 0, 1, 2, 3
+OK, INVALID, UNSUPPORTED, LAUNCH, SCRATCH = 0, 1, 2, 3, 4
 BF16, F32 = 1, 0
 FAKE = 0x1000  # a 16-byte aligned non-NULL address; never dereferenced here
 
@@ -42,6 +42,7 @@ def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"mha_forward", "mha_project_qkv", "mha_out_proj",
                                          "mha_self_attention_fused", "mha_forward_windowed",
                                          "mha_decode", "mha_decode_workspace_bytes",
+                                         "mha_decode_noalloc",
                                          "mha_out_proj_post_norm", "mha_status_string"}
 
 
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in (OK, INVALID, UNSUPPORTED, LAUNCH, 99):
+    for s in (OK, INVALID, UNSUPPORTED, LAUNCH, SCRATCH, 99):
         assert L.mha_status_string(s)
     assert L.mha_status_string(OK) == b"ok"
 
@@ -226,3 +227,26 @@ def test_post_norm_validation(L):
     assert call(h=1024, dv=1024, dm=1024) == UNSUPPORTED  # W^O of 2^30 elements
     assert call(B=0) == OK
     assert call(Lq=0, o=None) == OK
+
+
+def test_decode_noalloc_validation(L):
+    """The allocation-free decode step validates like mha_decode and refuses
+    problems whose partial states exceed the static scratch (16 MiB) before
+    any HIP call."""
+    N = L.mha_decode_noalloc
+    # (dt, B, h, L, dk, dv, q, k, v, lens, o, stream)
+    def call(**kw):
+        a = dict(dt=BF16, B=4, h=8, L=2000, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, lens=FAKE,
+                 o=FAKE)
+        a.update(kw)
+        return N(*a.values(), None)
+    assert call(dt=9) == INVALID
+    assert call(h=0) == INVALID
+    assert call(lens=None) == INVALID
+    assert call(o=FAKE + 4) == INVALID
+    assert call(dk=32, dv=32) == UNSUPPORTED
+    assert call(B=0) == OK
+    # 64 x 16 heads x 64 chunks x 66 floats = 17.3 MB > 16 MiB
+    assert L.mha_decode_workspace_bytes(64, 16, 65536, 64) > 16 << 20
+    assert call(B=64, h=16, L=65536) == SCRATCH
+    assert b"scratch" in L.mha_status_string(SCRATCH)

@@ -10,6 +10,7 @@ library raises at the first call.
     mha_forward(q, k, v, mask, kv_lens)          O = softmax(QK^T/sqrt(d_k) + M) V
     mha_forward(..., window=w)                    the same over keys |i - j| <= w only
     mha_decode(q, k_cache, v_cache, cache_lens)   one decoding step against a K/V cache
+    mha_decode_noalloc(q, k, v, lens, out)        the same with no allocation at all
     mha_project_qkv(x_q, x_kv, w_q, w_k, w_v, h)  Q, K, V = X_q W^Q, X_kv W^K, X_kv W^V
     mha_out_proj(o, w_o)                          Y = Concat(heads) W^O
     mha_out_proj_post_norm(o, w_o, x, g, b)       LayerNorm(x + Concat(heads) W^O)
@@ -68,6 +69,8 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.mha_forward_windowed.restype = i
     L.mha_decode.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, ctypes.c_size_t, p]
     L.mha_decode.restype = i
+    L.mha_decode_noalloc.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p]
+    L.mha_decode_noalloc.restype = i
     L.mha_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.mha_decode_workspace_bytes.restype = ctypes.c_size_t
     L.mha_project_qkv.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
@@ -198,6 +201,34 @@ def mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           _stream(q.device))
     if rc != 0:
         raise MHAError(rc, "mha_decode")
+    return out
+
+
+def mha_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       cache_lens: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """mha_decode with the library's static scratch instead of a workspace:
+    the call allocates nothing, so it may be captured in a HIP graph.  The
+    output tensor must be given.  Calls that overlap in time on one GPU
+    share the scratch and race."""
+    _check(q, "q")
+    _check(k_cache, "k_cache", q.dtype, q.device)
+    _check(v_cache, "v_cache", q.dtype, q.device)
+    _check(cache_lens, "cache_lens", torch.int32, q.device)
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be [B, 1, h, d]")
+    B, _, h, dk = q.shape
+    Lc = k_cache.shape[1]
+    dv = v_cache.shape[3]
+    if k_cache.shape != (B, Lc, h, dk) or v_cache.shape[:3] != (B, Lc, h):
+        raise ValueError("cache shape mismatch")
+    if cache_lens.shape != (B,):
+        raise ValueError(f"cache_lens must have shape ({B},)")
+    _check(out, "out", q.dtype, q.device, (B, 1, h, dv))
+    rc = lib().mha_decode_noalloc(_dtype_code(q), B, h, Lc, dk, dv, q.data_ptr(),
+                                  k_cache.data_ptr(), v_cache.data_ptr(), cache_lens.data_ptr(),
+                                  out.data_ptr(), _stream(q.device))
+    if rc != 0:
+        raise MHAError(rc, "mha_decode_noalloc")
     return out
 
 

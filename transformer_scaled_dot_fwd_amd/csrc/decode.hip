@@ -18,6 +18,8 @@
 //
 // Arithmetic is fp32 on the VALU: the scores stay in fp32 (no bf16 rounding
 // of p), and exp2 with log2(e) / sqrt(d_k) folded into q.
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -293,6 +295,39 @@ size_t decode_workspace_bytes(int B, int H, int L, int D) {
 }
 
 long long decode_partial_workgroups(int B, int L) { return (long long)B * n_splits(L); }
+
+// Scratch for callers that cannot allocate (mha_decode_noalloc): the fp32
+// partial states of one call, DECODE_SCRATCH_BYTES at most.  Each device
+// the library runs on holds its own copy until the process ends, and every
+// call on that device shares it.  Nothing in it needs clearing: the
+// partial-state kernel writes every state the merge reads.
+static __device__ __align__(256) float scratch[DECODE_SCRATCH_BYTES / sizeof(float)];
+
+// Device address of `scratch` on the stream's device, looked up with that
+// device current on the first call there and kept per device (the array's
+// host-side name is not a device address).  A lost race repeats the
+// lookup, which returns the same address.
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+    static std::atomic<void*> addr[64];
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = (cur != dev) ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (back != hipSuccess) return back;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
     const int hpl = heads_per_group(a.H);

@@ -54,6 +54,12 @@ size_t decode_workspace_bytes(int B, int H, int L, int D);
 long long decode_partial_workgroups(int B, int L);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// The library's static scratch for the decode step's partial states (for
+// callers that cannot allocate): its size, and its device address on the
+// stream's device.
+constexpr size_t DECODE_SCRATCH_BYTES = (size_t)16 << 20;
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 // The attention sub-layer's output with its residual and post-norm:
 // out[M, N] = LayerNorm(x[M, N] + o[M, K] w[K, N]) with gain gamma[N], bias
 // beta[N]; N in {256, 512, 1024}; bf16 (K % 32 == 0) or fp32.

@@ -8,6 +8,9 @@
 #include "launch.h"
 #include "mha.h"
 
+static_assert(MHA_DECODE_SCRATCH_BYTES == mha::DECODE_SCRATCH_BYTES,
+              "the header states the static scratch's size");
+
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -24,6 +27,8 @@ const char* mha_status_string(int status) {
         case MHA_ERR_INVALID_ARG: return "invalid argument";
         case MHA_ERR_UNSUPPORTED: return "unsupported dtype or shape (not compiled)";
         case MHA_ERR_LAUNCH: return "kernel launch failed";
+        case MHA_ERR_SCRATCH:
+            return "problem needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }
@@ -177,26 +182,58 @@ size_t mha_decode_workspace_bytes(int B, int h, int L_cache, int d_k) {
     return mha::decode_workspace_bytes(B, h, L_cache, d_k);
 }
 
-int mha_decode(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v, const void* q,
-               const void* k_cache, const void* v_cache, const int32_t* cache_lens, void* o,
-               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by mha_decode and mha_decode_noalloc (everything but the
+// workspace); MHA_OK means "launch".
+int decode_check(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v, const void* q,
+                 const void* k_cache, const void* v_cache, const int32_t* cache_lens,
+                 const void* o) {
     if (dt != MHA_F32 && dt != MHA_BF16) return MHA_ERR_INVALID_ARG;
     if (B < 0 || h < 1 || L_cache < 0 || d_k < 1 || d_v < 1) return MHA_ERR_INVALID_ARG;
     if (B == 0) return MHA_OK;
-    if (!q || !o || !cache_lens || !workspace) return MHA_ERR_INVALID_ARG;
+    if (!q || !o || !cache_lens) return MHA_ERR_INVALID_ARG;
     if (L_cache > 0 && (!k_cache || !v_cache)) return MHA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(o) || !aligned16(workspace) ||
+    if (!aligned16(q) || !aligned16(o) ||
         (L_cache > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
         return MHA_ERR_INVALID_ARG;
     if (dt != MHA_BF16 || d_k != d_v || (d_k != 64 && d_k != 128)) return MHA_ERR_UNSUPPORTED;
-    if (workspace_bytes < mha::decode_workspace_bytes(B, h, L_cache, d_k))
-        return MHA_ERR_INVALID_ARG;
     // One sequence's cache rows are addressed with 32-bit byte offsets; one
     // workgroup per (sequence, chunk of the cache).
     if ((long long)L_cache * h * d_k * 2 >= (1LL << 31)) return MHA_ERR_UNSUPPORTED;
     if (mha::decode_partial_workgroups(B, L_cache) > INT_MAX || (long long)B * h > INT_MAX)
         return MHA_ERR_UNSUPPORTED;
+    return MHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_decode(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v, const void* q,
+               const void* k_cache, const void* v_cache, const int32_t* cache_lens, void* o,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int rc = decode_check(dt, B, h, L_cache, d_k, d_v, q, k_cache, v_cache, cache_lens, o);
+    if (rc != MHA_OK || B == 0) return rc;
+    if (!workspace || !aligned16(workspace)) return MHA_ERR_INVALID_ARG;
+    if (workspace_bytes < mha::decode_workspace_bytes(B, h, L_cache, d_k))
+        return MHA_ERR_INVALID_ARG;
     mha::DecodeArgs a{B, h, L_cache, d_k, q, k_cache, v_cache, cache_lens, o, workspace};
+    return launch_status(mha::launch_decode_bf16(a, stream));
+}
+
+int mha_decode_noalloc(mha_dtype dt, int B, int h, int L_cache, int d_k, int d_v,
+                       const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cache_lens, void* o, hipStream_t stream) {
+    const int rc = decode_check(dt, B, h, L_cache, d_k, d_v, q, k_cache, v_cache, cache_lens, o);
+    if (rc != MHA_OK || B == 0) return rc;
+    if (mha::decode_workspace_bytes(B, h, L_cache, d_k) > MHA_DECODE_SCRATCH_BYTES)
+        return MHA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (mha::decode_scratch(stream, &ws) != hipSuccess) return MHA_ERR_LAUNCH;
+    mha::DecodeArgs a{B, h, L_cache, d_k, q, k_cache, v_cache, cache_lens, o, ws};
     return launch_status(mha::launch_decode_bf16(a, stream));
 }
 
