@@ -804,7 +804,7 @@ def main():
     sweep = attention_sweep(dev, args.steps, args.warmup)
     rows8 = {r.name for r in configs.metric_rows()}
     dom = max((e for e in sweep if e["workload"] in rows8), key=lambda e: e["us"])
-    roofline = {"kernel": "attn_fwd_bf16 (streaming attention, d=64)",
+    roofline = {"kernel": "attn_stream_bf16 (streaming attention, d=64)",
                 "workload": dom["workload"], "bound": "mfma",
                 "achieved": round(dom["flops"] / (dom["us"] * 1e-6) / 1e12, 1),
                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",

@@ -42,11 +42,13 @@ class Case:
     dtype: str = "bf16"
     window: Optional[int] = None
     sampled: bool = False   # compare sampled rows (the oracle's full run is slow)
+    huge: bool = False      # the staircase that climbs ~188 base-2 units
 
     def label(self):
         w = "" if self.window is None else f" w={self.window}"
+        hg = " huge" if self.huge else ""
         return (f"{self.name} B={self.B} h={self.h} Lq={self.Lq} Lk={self.Lk} d={self.d} "
-                f"mask={self.mask}{w} {self.dtype}")
+                f"mask={self.mask}{w} {self.dtype}{hg}")
 
 
 def _cases():
@@ -57,14 +59,11 @@ def _cases():
         # at most 256 keys: eight tiles
         out.append(Case("short rows NT=8", 3, 2, 256 if m & CAUSAL else 200, 256, 64, m))
     for m in (NONE, CAUSAL, PAD | CAUSAL):
-        # streaming kernel, 32 queries per wave
-        out.append(Case("long rows QB=1", 2, 2, 700, 700, 64, m))
-    # streaming kernel, 64 queries per wave: causal rows above 2048, and
-    # non-causal rows above 512 whose workgroups (two per CU, 256 CUs)
-    # fill at least 90% of their last round: 2 * 80 * 3 = 480 of 512
-    out.append(Case("long rows QB=2 causal", 1, 2, 2200, 2200, 64, CAUSAL))
-    out.append(Case("long rows QB=2", 2, 80, 768, 768, 64, NONE, sampled=True))
-    out.append(Case("long rows QB=2 padded", 2, 80, 768, 768, 64, PAD, sampled=True))
+        # the streaming kernel (rows above 256 keys)
+        out.append(Case("long rows", 2, 2, 700, 700, 64, m))
+    out.append(Case("long rows causal", 1, 2, 2200, 2200, 64, CAUSAL))
+    out.append(Case("long rows, many heads", 2, 80, 768, 768, 64, NONE, sampled=True))
+    out.append(Case("long rows, many heads, padded", 2, 80, 768, 768, 64, PAD, sampled=True))
     for d in (16, 32, 128):
         for m in (NONE, CAUSAL):
             out.append(Case(f"head size {d}", 2, 2, 600, 600, d, m))
@@ -74,6 +73,24 @@ def _cases():
     for m in (NONE, CAUSAL, PAD):
         out.append(Case("fp32", 2, 2, 300, 300, 64, m, dtype="f32"))
     return out
+
+
+def _huge_cases():
+    """The huge staircase through the streaming kernels (rows longer than
+    256 keys): its rows climb far enough above their first tiles that a
+    reference fixed there would overflow."""
+    out = []
+    for m in (NONE, PAD, CAUSAL, PAD | CAUSAL):
+        out.append(Case("long rows", 2, 2, 700, 700, 64, m, huge=True))
+    out.append(Case("long rows causal", 1, 2, 2200, 2200, 64, CAUSAL, huge=True))
+    for m in (NONE, CAUSAL):
+        out.append(Case("restricted attention", 2, 2, 1024, 1024, 64, m, window=300, huge=True))
+    for d in (16, 32, 128):
+        out.append(Case(f"head size {d}", 2, 2, 600, 600, d, CAUSAL, huge=True))
+    return out
+
+
+HUGE_CASES = _huge_cases()
 
 
 CASES = _cases()
@@ -89,7 +106,10 @@ def inputs(c: Case, seed: int):
     q = generate.normal((c.B, c.Lq, c.h, c.d), seed, c.dtype)
     k = generate.normal((c.B, c.Lk, c.h, c.d), seed + 1, c.dtype)
     v = generate.normal((c.B, c.Lk, c.h, c.d), seed + 2, c.dtype)
-    q, k = generate.staircase(q, k)
+    if c.huge:
+        q, k = generate.staircase(q, k, levels=generate.STAIRCASE_HUGE_LEVELS)
+    else:
+        q, k = generate.staircase(q, k)
     return q, k, v, (lengths(c) if c.mask & PAD else None)
 
 
@@ -110,3 +130,25 @@ def growths(s: np.ndarray) -> np.ndarray:
         g = tmax[..., 1:] - prev
     ok = np.isfinite(prev) & np.isfinite(g)
     return g[ok]
+
+
+def climbs(s: np.ndarray, first_tiles: int = 1) -> np.ndarray:
+    """s: scaled logits [..., Lq, Lk] (-inf at masked pairs).  For every
+    row with a legal key, how far (base-2 units) its maximum rises above
+    the maximum of its first `first_tiles` 32-key tiles that hold a legal
+    key."""
+    s = np.asarray(s, dtype=np.float64) * LOG2E
+    Lk = s.shape[-1]
+    nt = (Lk + KT - 1) // KT
+    pad = nt * KT - Lk
+    if pad:
+        s = np.concatenate([s, np.full(s.shape[:-1] + (pad,), -np.inf)], axis=-1)
+    tmax = s.reshape(-1, nt, KT).max(axis=-1)          # [rows, nt]
+    out = []
+    for row in tmax:
+        legal = np.nonzero(np.isfinite(row))[0]
+        if legal.size == 0:
+            continue
+        first = row[legal[0]:legal[0] + first_tiles].max()
+        out.append(row.max() - first)
+    return np.array(out)

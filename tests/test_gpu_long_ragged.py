@@ -1,11 +1,8 @@
-"""Long rows with ragged tails, in the launch configurations that only long
-rows reach.
+"""Long rows with ragged tails in the streaming kernel (rows above 256 keys).
 
-The long-row attention kernel runs 64 queries per wave for non-causal rows
-(longer than 512) whose workgroups fill their last round on the CUs, and
-for causal rows longer than 2048; otherwise 32 per wave.  The sweep
-shapes are multiples of 256, so these cases put ragged query and key tails
-(and cross-attention, Lq != Lk) into both variants.  The oracle evaluates
+The sweep shapes are multiples of 256 (the streaming kernel's queries per
+workgroup) and of its 32-key tiles, so these cases put ragged query and key
+tails, and cross-attention (Lq != Lk), through it.  The oracle evaluates
 sampled rows one by one (oracle_attention_rows) on the full-size inputs,
 including each sequence's last query row.
 """
@@ -22,9 +19,8 @@ pytestmark = pytest.mark.gpu
 
 NONE, PAD, CAUSAL = mha.MASK_NONE, mha.MASK_KEY_PADDING, mha.MASK_CAUSAL
 
-# (B, h, Lq, Lk, masks): 64 queries per wave (B h ceil(Lq / 256) = 504
-# workgroups, one full round on 256 CUs; causal above 2048), then 32 per wave
-# on a long cross-attention.
+# (B, h, Lq, Lk, masks): long cross-attention and self-attention with ragged
+# query and key tails.
 CASES = [(7, 8, 2100, 3000, (NONE, PAD)), (2, 4, 2300, 2300, (CAUSAL, PAD | CAUSAL)),
          (3, 4, 700, 1900, (NONE, PAD))]
 

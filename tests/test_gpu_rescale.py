@@ -19,7 +19,7 @@ import torch
 import oracle
 import transformer_scaled_dot_fwd_amd as mha
 from gpu_util import check, device, say, to_np
-from rescale_cases import CASES, growths, inputs
+from rescale_cases import CASES, HUGE_CASES, climbs, growths, inputs
 from workloads import generate
 
 pytestmark = pytest.mark.gpu
@@ -123,3 +123,21 @@ def test_rescale_across_decode_chunks(d):
         torch.cuda.synchronize()
         check(o, oracle.attention(qr, k, v, mask=1, kv_lens=lens), "bf16",
               f"decode d={d} amplitude {generate.STAIRCASE_AMPS[row]}")
+
+
+@pytest.mark.parametrize("case", HUGE_CASES, ids=lambda c: c.label())
+def test_rows_climbing_past_the_fp32_range(case):
+    """Rows whose maximum climbs ~188 base-2 units above their first tiles:
+    the streaming kernel's reference, fixed at the first tiles, would
+    overflow for them, so they take the recomputation with a moving
+    reference; their neighbours in the same waves keep their results."""
+    dev = device()
+    say(f"case climb {case.label()}")
+    q, k, v, lens = inputs(case, 7400)
+    o = mha.mha_forward(q.to(dev), k.to(dev), v.to(dev), mask=case.mask,
+                        kv_lens=None if lens is None else lens.to(dev), window=case.window)
+    torch.cuda.synchronize()
+    ref, s = oracle.attention(q, k, v, mask=case.mask, kv_lens=lens, window=case.window,
+                              return_s=True)
+    assert (climbs(s, 3 if case.window is not None else 1) > 130).sum() > 0
+    check(o, ref, case.dtype, case.label())

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libmha.so")
-SOURCES = ["attention.hip", "decode.hip", "fused.hip", "gemm.hip", "mha_api.hip", "norm.hip"]
+SOURCES = ["attention.hip", "attn_stream.hip", "decode.hip", "fused.hip", "gemm.hip", "mha_api.hip", "norm.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -12,17 +12,15 @@
 // and running sum l, rescaling the partial output when m grows), which is
 // the exact identity softmax(x) = softmax(x - c) applied tile by tile; the
 // score matrix never leaves registers.
-#include <atomic>
-
 #include "device.h"
 #include "launch.h"
 
 namespace mha {
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA path, head size D in {16, 32, 64, 128} (the base shape's 64 and
-// the other head shapes of "Paper Deep Reading", section 08, Table 3, rows
-// (A)).
+// bf16 MFMA path for the other head shapes of "Paper Deep Reading", section
+// 08, Table 3, rows (A): D in {16, 32, 128} (the template also takes 64; the
+// base shape's d = 64 streams through attn_stream.hip).
 //
 // Workgroup = NW waves = one (batch row, head, tile of 32*QB*NW queries).
 // Wave w owns QB blocks of 32 consecutive queries, one query per lane
@@ -866,42 +864,19 @@ hipError_t launch_short_bf16(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Compute units of the device the stream belongs to (the current device for
-// the null stream), queried once per device (a lost race only repeats the
-// query).  Only the choice between two tilings depends on it.
-int device_cu_count(hipStream_t stream) {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n > 0) return n;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-        n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
 }  // namespace
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
-    // Four waves per workgroup share each K/V tile.  Short rows, and causal
-    // rows up to 2048, run 32 queries per wave: twice the workgroups and
-    // three per CU, which hides load latency and evens out the causal
-    // triangle.  Longer rows run 64 queries per wave, halving the LDS reads
-    // per MFMA, where that pays: non-causal rows whose workgroups (two per
-    // CU) fill at least 90% of their last round on the CUs, and causal rows
-    // above 2048; a partial last round leaves CUs idle, and 32 queries per
-    // wave finishes first.
-    // Rows of at most 128 (256) keys: the whole K/V row in LDS at once.
-    // Head sizes other than 64 run the long-row kernel at every length, 32
-    // queries per wave.
-    if (a.window >= 0) {  // restricted attention: the long-row kernel's band variant
+    // d = 64: rows of at most 128 (256) keys hold the whole K/V row in LDS
+    // at once; longer rows and restricted attention stream through the
+    // kernel of attn_stream.hip.  Other head sizes run this file's
+    // streaming kernel at every length, 32 queries per wave.
+    if (a.window >= 0) {  // restricted attention: the streaming kernels' band variants
         switch (a.D) {
             case 16: return launch_bf16<16, ATTN_NW, 1, true>(a, stream);
             case 32: return launch_bf16<32, ATTN_NW, 1, true>(a, stream);
             case 128: return launch_bf16<128, 8, 1, true>(a, stream);
-            default: return launch_bf16<64, ATTN_NW, 1, true>(a, stream);
+            default: return launch_attention_stream_bf16(a, stream);
         }
     }
     switch (a.D) {
@@ -912,15 +887,7 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     }
     if (a.Lk <= 128) return launch_short_bf16<4>(a, stream);
     if (a.Lk <= 256) return launch_short_bf16<8>(a, stream);
-    const bool causal = (a.mask & 2) != 0;  // AttnArgs::mask bit 1
-    if (a.Lq <= 512 || (causal && a.Lq <= 2048)) return launch_bf16<64, ATTN_NW, 1>(a, stream);
-    if (!causal) {
-        const long wg = (long)a.B * a.H * ((a.Lq + 255) / 256);
-        const long slots = 2L * device_cu_count(stream);
-        const long rounds = (wg + slots - 1) / slots;
-        if (wg * 10 < rounds * slots * 9) return launch_bf16<64, ATTN_NW, 1>(a, stream);
-    }
-    return launch_bf16<64, ATTN_NW, 2>(a, stream);
+    return launch_attention_stream_bf16(a, stream);
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {

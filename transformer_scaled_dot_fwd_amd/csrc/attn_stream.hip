@@ -1,0 +1,607 @@
+// attn_stream.hip -- streaming scaled dot-product attention forward for
+// gfx950, d = 64, rows longer than the whole-row-in-LDS kernel takes:
+//
+//   O = softmax(Q K^T / sqrt(d_k) + M) V        for every (batch row, head)
+//
+// ("Paper Deep Reading: Attention Is All You Need", section 04, attention
+// equation with the mask M; MatMul -> Scale -> Mask -> SoftMax -> MatMul as
+// in Figure 2, left.)  M is -inf at illegal pairs: keys at or beyond the
+// batch row's length, keys after the query (decoder), and, for restricted
+// self-attention (section 05, complexity table), keys more than `window`
+// positions from the query.
+//
+// The softmax runs over 32-key tiles against a reference value m per query
+// row: p = exp2((s - m) log2(e) / sqrt(d)), acc += p v, l += p, and O = acc
+// / l at the end.  This is the exact identity softmax(x) = softmax(x - c)
+// for any c; m only has to keep p inside the fp32/bf16 range.  m is the
+// row maximum over the wave's first tile (its first three under restricted
+// attention, where a row's band may start up to two tiles in), found
+// exactly, and then stays fixed: a later key would have to exceed it by
+// more than ~88 scaled-logit units (2^127 in p) to overflow.  A row whose
+// sum or output is not finite at the end (that overflow, or a row with no
+// legal key in its first tiles) is recomputed by the wave with a running
+// maximum that moves every tile.  The common path thereby carries no
+// per-tile row maximum and no per-tile data-dependent branch (a branch on
+// a VALU compare waits for the wave's MFMAs in flight): only the scale and
+// offset, the exponential, the rounding and the row-sum step per value,
+// which with the MFMAs is the work this kernel is bound by at d = 64.
+//
+// Workgroup = 4 waves = one (batch row, head, block of 256 queries); wave w
+// owns 64 queries (two blocks of 32, one query per lane column).  K/V tiles
+// of 32 rows reach LDS by direct global-to-LDS loads into a 6-stage ring,
+// issued four tiles ahead, one barrier per tile.  Per tile j a wave issues
+//
+//   O^T += V_{j-1}^T P_{j-1}^T   8 MFMAs (the previous tile's weights)
+//   S_{j+1}^T = K_{j+1} Q^T      8 MFMAs (the next tile's scores)
+//
+// one per slot, each beside one step of the softmax of S_j, so the matrix
+// core runs while the VALU does the softmax.
+#include "device.h"
+#include "launch.h"
+
+namespace mha {
+namespace {
+
+constexpr int SD = 64;                 // head size
+constexpr int SKT = 32;                // keys per tile
+constexpr int SNS = 6;                 // LDS ring stages
+constexpr int SNW = 4;                 // waves per workgroup
+constexpr int STILE = SKT * SD * 2;    // bytes of one K (or V) tile: 32 rows of 128 bytes
+constexpr int SSTAGE = 2 * STILE;      // K tile, then V tile
+constexpr float L_LIMIT = 1.0e30f;    // a finite row sum at most this is not an overflow
+
+// Tiles from a wave's first whose rows set their reference exactly: the
+// first tile holds every row's first legal key (key 0), except under
+// restricted attention, where the band of the wave's last row (63 rows on)
+// starts up to two tiles later.
+template <bool WIN>
+constexpr int stream_init_tiles() {
+    return WIN ? 3 : 1;
+}
+
+// Query blocks of 32 per wave (QB = 1 or 2) and the workgroups per CU the
+// register budget then allows.
+template <int QB>
+constexpr int stream_occupancy() {
+    return QB == 1 ? 3 : 2;
+}
+
+template <int QB, bool PAD, bool CAUSAL, bool WIN>
+__global__ __launch_bounds__(256, stream_occupancy<QB>()) void attn_stream_bf16(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
+    int n_qtiles, float scale_log2e, int window) {
+    __shared__ __attribute__((aligned(1024))) char smem[SNS * SSTAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+
+    // Workgroup -> (batch row, head, query block).  Workgroups go to the 8
+    // XCDs round-robin (workgroup w on XCD w % 8); when B*H divides by 8,
+    // XCD x gets the (batch row, head) pairs x*nbh/8 .. (x+1)*nbh/8 - 1
+    // whole, so every query block of a pair shares that XCD's L2 for its
+    // K/V.  Causal: within each XCD the longest query blocks start first.
+    constexpr int SQB = QB;                // 32-query blocks per wave
+    constexpr int SWQ = 32 * SQB;          // queries per wave
+    constexpr int SBM = SWQ * SNW;         // queries per workgroup
+    constexpr int NSL = 8 * SQB;           // slots (and MFMAs) per tile
+    constexpr int SNI = stream_init_tiles<WIN>();
+    const int nbh = B * H;
+    const int w = (int)blockIdx.x;
+    int bh, qt;
+    if ((nbh & 7) == 0) {
+        const int x = w & 7, slot = w >> 3, per = nbh >> 3;
+        if (CAUSAL) {
+            qt = n_qtiles - 1 - slot / per;
+            bh = x * per + slot % per;
+        } else {
+            bh = x * per + slot / n_qtiles;
+            qt = slot % n_qtiles;
+        }
+    } else if (CAUSAL) {
+        qt = n_qtiles - 1 - w / nbh;
+        bh = w % nbh;
+    } else {
+        bh = w / n_qtiles;
+        qt = w % n_qtiles;
+    }
+    const int b = bh / H;
+    const int hh = bh - b * H;
+    const int q0 = qt * SBM;
+
+    int kv_end = Lk;
+    if (PAD) kv_end = min(max(kv_lens[b], 0), Lk);
+    int key_end = kv_end;
+    if (CAUSAL) key_end = min(key_end, min(q0 + SBM, Lq));
+    // The workgroup streams tiles t_first .. n_tiles - 1 (a band around its
+    // queries when WIN; window < Lk, so no sum below overflows).
+    int t_first = 0;
+    if (WIN) {
+        key_end = min(key_end, q0 + SBM + window);
+        t_first = max(q0 - window, 0) / SKT;
+    }
+    const int n_tiles = (key_end + SKT - 1) / SKT;
+    const int n_loop = max(n_tiles - t_first, 0);
+
+    // Tiles this wave computes, w_first .. n_mine - 1: none if it holds no
+    // query row; causal stops at the tile holding the wave's last query; a
+    // band starts and stops a window away from the wave's queries.
+    const int wq0 = q0 + SWQ * wave;
+    int n_mine = (wq0 < Lq) ? n_tiles : 0;
+    if (CAUSAL) n_mine = min(n_mine, (wq0 + SWQ + SKT - 1) / SKT);
+    int w_first = t_first;
+    if (WIN) {
+        n_mine = min(n_mine, (min(kv_end, wq0 + SWQ + window) + SKT - 1) / SKT);
+        w_first = max(wq0 - window, 0) / SKT;
+    }
+
+    const size_t rs = (size_t)H * SD;  // elements between consecutive positions
+    const uint32_t rsb = (uint32_t)(rs * sizeof(bf16));
+    const bf16* qp = q + ((size_t)b * Lq * H + hh) * SD;
+    const bf16* kp = k + ((size_t)b * Lk * H + hh) * SD;
+    const bf16* vp = v + ((size_t)b * Lk * H + hh) * SD;
+    bf16* op = o + ((size_t)b * Lq * H + hh) * SD;
+
+    bf16x8 qop[SQB][4];  // Q as the B operand of S^T = K Q^T (loaded in the prologue)
+
+    // Direct global-to-LDS tile loads: thread tid fills chunk position tid
+    // of a tile (row tid / 8), fetching the chunk the swizzle puts there;
+    // rows at or past kv_end land as zeros without a memory access.
+    const uint32_t kv_bytes = kv_end > 0 ? (uint32_t)(kv_end - 1) * rsb + SD * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kp, kv_bytes);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vp, kv_bytes);
+    const int pr = tid >> 3, pc = tid & 7;
+    const uint32_t k_dma = (uint32_t)pr * rsb + 16 * (pc ^ k_swz(pr));
+    const uint32_t v_dma = (uint32_t)pr * rsb + 16 * (pc ^ v_swz(pr));
+    const uint32_t tile_gbytes = (uint32_t)SKT * rsb;
+    const uint32_t lds_wave = lds_addr(smem) + 1024 * wave;
+    // Tile t (of the workgroup's stream, jr = t - t_first) into stage jr % SNS.
+    auto dma = [&](int jr) {
+        const int t = t_first + jr;
+        const uint32_t base = t < n_tiles ? (uint32_t)t * tile_gbytes : OOB_OFFSET;
+        const uint32_t st = lds_wave + (uint32_t)(jr % SNS) * SSTAGE;
+        load_lds16(krsrc, st, base + k_dma);
+        load_lds16(vrsrc, st + STILE, base + v_dma);
+    };
+
+    // LDS operand offsets inside a stage (same lane patterns as the
+    // whole-row kernel): K rows for S^T, V^T by transpose reads.
+    uint32_t k_rd[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = l32 * 128 + 16 * ((2 * kk + half) ^ k_swz(l32));
+    uint32_t v_rd[2];
+    {
+        const int row = 4 * half + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            const int chunk = 4 * db + 2 * (g & 1) + ((i16 & 3) >> 1);
+            v_rd[db] = STILE + row * 128 + 16 * (chunk ^ v_swz(row)) + 8 * (i16 & 1);
+        }
+    }
+    auto read_k = [&](int stage, bf16x8 (&ka)[4]) {
+        const char* base = smem + stage * SSTAGE;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[kk] = *(const bf16x8*)(base + k_rd[kk]);
+    };
+    // V^T operands [16-key chunk][d block] of the tile in `stage`.
+    auto read_vt = [&](int stage, bf16x8 (&va)[2][2]) {
+        const char* base = smem + stage * SSTAGE;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+                va[c][db] = join(lds_read_tr((const bf16*)(base + 2048 * c + v_rd[db])),
+                                 lds_read_tr((const bf16*)(base + 2048 * c + v_rd[db] + 1024)));
+    };
+
+    f32x16 acc[SQB][2];
+#pragma unroll
+    for (int qb = 0; qb < SQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
+    // Per query row (this lane's column): the reference m (raw logit units),
+    // m * scale_log2e, and this lane's share of the row sum.
+    float m_run[SQB], mc[SQB], l_part[SQB];
+#pragma unroll
+    for (int qb = 0; qb < SQB; ++qb) {
+        m_run[qb] = -INFINITY;
+        mc[qb] = -INFINITY;
+        l_part[qb] = 0.0f;
+    }
+    const f32x16 zero16 = {};
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+    // Mask S_j (boundary tiles only): -inf at illegal pairs.
+    auto mask_tile = [&](int j, f32x16 (&S)[SQB]) {
+        const int k0 = j * SKT;
+        const bool need = (k0 + SKT > kv_end) || (CAUSAL && k0 + SKT - 1 > wq0) ||
+                          (WIN && (k0 < wq0 + SWQ - 1 - window || k0 + SKT - 1 > wq0 + window));
+        if (!need) return;
+#pragma unroll
+        for (int qb = 0; qb < SQB; ++qb) {
+            const int qi = wq0 + 32 * qb + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + acc_row(r, half);
+                bool legal = key < kv_end;
+                if (CAUSAL) legal = legal && key <= qi;
+                if (WIN) legal = legal && key >= qi - window && key <= qi + window;
+                S[qb][r] = legal ? S[qb][r] : -INFINITY;
+            }
+        }
+    };
+
+    // The reference of tile j's rows when it moves (the wave's first tiles,
+    // and every tile of the recomputation): the running maximum over the
+    // tile's legal values; acc and l are rescaled by exp2(m_old - m_new)
+    // (0 while nothing has accumulated; 1 while a row has no legal key).
+    // Returns the factors, which the caller applies to acc once the
+    // previous tile's PV has landed in it.
+    auto move_reference = [&](const f32x16 (&S)[SQB], float (&alpha)[SQB]) {
+#pragma unroll
+        for (int qb = 0; qb < SQB; ++qb) {
+            float mx = S[qb][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[qb][r]);
+            mx = max_halves(mx);
+            const float m_new = fmaxf(m_run[qb], mx);
+            alpha[qb] = (m_new == -INFINITY || m_new == m_run[qb])
+                            ? 1.0f
+                            : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * scale_log2e);
+            m_run[qb] = m_new;
+            mc[qb] = m_new * scale_log2e;
+        }
+    };
+    auto rescale = [&](const float (&alpha)[SQB]) {
+#pragma unroll
+        for (int qb = 0; qb < SQB; ++qb) {
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha[qb];
+            l_part[qb] *= alpha[qb];
+        }
+    };
+
+    // One tile j of the pipeline: 8 slots per query block, each issuing one
+    // MFMA and one step of the softmax for four pairs of S_j's values at
+    // once.  Pair n is values 2(n%8), 2(n%8)+1 of query block n/8; its four
+    // steps --
+    // scale and offset (two FMAs), two exponentials, the rounding to a
+    // packed bf16 pair in Pcur, the row-sum step -- run in slots n-2 ..
+    // n+1, so no instruction waits for the one just before it.  The MFMAs:
+    // the middle half of the slots the scores of tile j+1 (k slice, query
+    // block), late enough for the K rows to have arrived from LDS and early
+    // enough to be done when the next tile's first values are read; the
+    // first and last quarters the PV of tile j-1 from Pprev (16-key chunk 0,
+    // then 1; query block, d block).  The wave's first SNI tiles (`exact`, a
+    // wave-uniform flag) move the reference first.
+    auto tile_step = [&](bool exact, int j, int stage_next, f32x16 (&Scur)[SQB],
+                         f32x16 (&Snext)[SQB], const bf16x8 (&Pprev)[SQB][2],
+                         bf16x8 (&Pcur)[SQB][2], const bf16x8 (&va)[2][2]) {
+        bf16x8 ka[4];
+        read_k(stage_next, ka);
+        mask_tile(j, Scur);
+        float alpha[SQB], off[SQB];
+        if (exact) move_reference(Scur, alpha);
+        // Rows with no reference yet (no legal key so far) keep mc = -inf,
+        // which in the common path turns any value they meet into inf or
+        // NaN, so such a row ends non-finite and is recomputed; the exact
+        // tiles give them weight 0 (all their values are -inf) instead.
+#pragma unroll
+        for (int qb = 0; qb < SQB; ++qb)
+            off[qb] = (exact && m_run[qb] == -INFINITY) ? 0.0f : mc[qb];
+        float lt[SQB];
+        float xs[NSL][2], ex[NSL][2];
+        bf16x2 pk[NSL];
+        auto step_fma = [&](int n) {
+            if (n < 0 || n >= NSL) return;
+            const int qb = n >> 3, i = n & 7;
+            xs[n][0] = __builtin_fmaf(Scur[qb][2 * i], scale_log2e, -off[qb]);
+            xs[n][1] = __builtin_fmaf(Scur[qb][2 * i + 1], scale_log2e, -off[qb]);
+        };
+        auto step_exp = [&](int n) {
+            if (n < 0 || n >= NSL) return;
+            ex[n][0] = __builtin_amdgcn_exp2f(xs[n][0]);
+            ex[n][1] = __builtin_amdgcn_exp2f(xs[n][1]);
+        };
+        auto step_round = [&](int n) {
+            if (n < 0 || n >= NSL) return;
+            const int qb = n >> 3, i = n & 7;
+            pk[n] = bf16x2{(bf16)ex[n][0], (bf16)ex[n][1]};
+            Pcur[qb][i >> 2][2 * (i & 3)] = pk[n][0];
+            Pcur[qb][i >> 2][2 * (i & 3) + 1] = pk[n][1];
+        };
+        auto step_sum = [&](int n) {
+            if (n < 0 || n >= NSL) return;
+            const int qb = n >> 3, i = n & 7;
+            lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk[n], ones, i == 0 ? 0.0f : lt[qb], false);
+        };
+        step_fma(0);
+        step_fma(1);
+        step_exp(0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < NSL + 1; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (s >= 2 * SQB && s < 6 * SQB) {
+                const int m = s - 2 * SQB, kk = m / SQB, qb = m % SQB;
+                Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
+            } else if (s < NSL) {
+                const int pv = s < 2 * SQB ? s : s - 4 * SQB;
+                const int c = pv / (2 * SQB), qb = (pv >> 1) % SQB, db = pv & 1;
+                acc[qb][db] = mfma32(va[c][db], Pprev[qb][c], acc[qb][db]);
+            }
+            step_fma(s + 2);
+            step_exp(s + 1);
+            step_round(s);
+            step_sum(s - 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        if (exact) rescale(alpha);  // acc now holds tile j-1's PV
+#pragma unroll
+        for (int qb = 0; qb < SQB; ++qb) l_part[qb] += lt[qb];
+    };
+
+    // ---- prologue: tiles 0 .. SNS-3 and Q in flight together, then all
+    // of them waited for.  (The tile loads are inline asm, invisible to the
+    // compiler's wait bookkeeping; with Q's loads retired before the loop,
+    // the waits it places for them stay out of the loop, where they would
+    // also wait for the tile loads in flight.)
+#pragma unroll
+    for (int jr = 0; jr < SNS - 2; ++jr) dma(jr);
+    // Q as the B operand of S^T = K Q^T: block qb, lane holds query
+    // wq0 + 32qb + l32, d = 16kk + 8half .. +7.  Rows past Lq read zeros.
+    const __amdgpu_buffer_rsrc_t qrsrc =
+        make_rsrc(qp, (uint32_t)(((size_t)(Lq - 1) * rs + SD) * sizeof(bf16)));
+#pragma unroll
+    for (int qb = 0; qb < SQB; ++qb) {
+        const int qi = wq0 + 32 * qb + l32;
+        const uint32_t qoff = qi < Lq ? (uint32_t)qi * rsb + 16 * half : OOB_OFFSET;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
+    }
+    // Q's values are consumed here, so the compiler's own wait for them
+    // (which also covers the tile loads issued before them) lands here.
+#pragma unroll
+    for (int qb = 0; qb < SQB; ++qb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(qop[qb][kk]));
+
+    f32x16 SA[SQB], SB[SQB];
+    // Weights of alternate tiles (the previous tile's wait for their PV);
+    // V^T of tile j-1.
+    bf16x8 PA[SQB][2], PB[SQB][2], va[2][2];
+#pragma unroll
+    for (int qb = 0; qb < SQB; ++qb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            PA[qb][c] = zero_bf16x8();
+            PB[qb][c] = zero_bf16x8();
+        }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) va[c][db] = zero_bf16x8();
+
+    // Iteration jr (tile j = t_first + jr, stage jr % SNS): the tiles up to
+    // j + 1 have landed (each thread waits for its own loads of them, the
+    // barrier for everyone's) and every wave is done with tile j - 2's
+    // stage, which the load of tile j + SNS - 2 then takes.  The loop body
+    // is unrolled over the ring so every LDS offset is an immediate; the
+    // score and weight register sets alternate with the tile's parity.
+    auto iteration = [&](int jr, f32x16 (&Scur)[SQB], f32x16 (&Snext)[SQB],
+                         const bf16x8 (&Pprev)[SQB][2], bf16x8 (&Pcur)[SQB][2], int stage) {
+        wait_vmcnt<2 * (SNS - 4)>();
+        barrier_lds();
+        dma(jr + SNS - 2);
+        const int j = t_first + jr;
+        if (j == w_first && j < n_mine) {
+            // the wave's first tile: its scores straight from the ring
+            bf16x8 ka[4];
+            read_k(stage, ka);
+#pragma unroll
+            for (int qb = 0; qb < SQB; ++qb) {
+                Scur[qb] = mfma32(ka[0], qop[qb][0], zero16);
+#pragma unroll
+                for (int kk = 1; kk < 4; ++kk) Scur[qb] = mfma32(ka[kk], qop[qb][kk], Scur[qb]);
+            }
+        }
+        if (j >= w_first && j < n_mine) {
+            tile_step(j < w_first + SNI, j, (stage + 1) % SNS, Scur, Snext, Pprev, Pcur, va);
+            read_vt(stage, va);  // V^T of tile j, for its PV in the next tile
+        }
+    };
+    for (int jr = 0; jr < n_loop; jr += SNS) {
+        iteration(jr, SA, SB, PB, PA, 0);
+        if (jr + 1 < n_loop) iteration(jr + 1, SB, SA, PA, PB, 1);
+        if (jr + 2 < n_loop) iteration(jr + 2, SA, SB, PB, PA, 2);
+        if (jr + 3 < n_loop) iteration(jr + 3, SB, SA, PA, PB, 3);
+        if (jr + 4 < n_loop) iteration(jr + 4, SA, SB, PB, PA, 4);
+        if (jr + 5 < n_loop) iteration(jr + 5, SB, SA, PA, PB, 5);
+    }
+    // Drain: the PV of the wave's last tile (zero weights if it had none),
+    // whose weights sit in the set of that tile's parity.
+    wait_vmcnt<0>();
+    const bool last_odd = n_mine > w_first && ((n_mine - 1 - t_first) & 1) != 0;
+#pragma unroll
+    for (int qb = 0; qb < SQB; ++qb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const bf16x8 pl = last_odd ? PB[qb][c] : PA[qb][c];
+#pragma unroll
+            for (int db = 0; db < 2; ++db) acc[qb][db] = mfma32(va[c][db], pl, acc[qb][db]);
+        }
+
+    // ---- epilogue: O = acc / l, or 0 for a row with no legal key.  A row
+    // whose sum or outputs are not finite (or whose sum exceeds L_LIMIT) is
+    // not stored here but recomputed below; the two lanes holding a row
+    // decide together.  Each store is an 8-byte piece of a query's row, 32
+    // rows per instruction; plain stores let L2 merge a row's pieces into
+    // whole lines.
+    auto finish = [&](int qb, bool store_ok) -> bool {
+        const float l_tot = sum_halves(l_part[qb]);
+        const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+        bf16x4 out[2][4];
+        bool ok = l_tot <= L_LIMIT;  // false for inf and NaN
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = acc[qb][db][4 * rg + e] * inv;
+                    ok = ok && __builtin_fabsf(x) <= 3.0e38f;
+                    out[db][rg][e] = (bf16)x;
+                }
+        const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
+        const bool redo = ((bad >> lane) | (bad >> (lane ^ 32))) & 1;
+        const int qi = wq0 + 32 * qb + l32;
+        if (qi < Lq && (store_ok || !redo)) {
+            bf16* orow = op + (size_t)qi * rs;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg)
+                    *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * half) = out[db][rg];
+        }
+        return redo;
+    };
+    bool redo[SQB];
+#pragma unroll
+    for (int qb = 0; qb < SQB; ++qb) redo[qb] = finish(qb, false);
+
+    // ---- recomputation of the rows that overflowed (rare: a key more than
+    // ~88 scaled-logit units above the row's first tiles), with a reference
+    // that moves every tile.  The wave streams its tiles alone through its
+    // own stage of the ring (the barrier: every wave is done with the ring),
+    // one tile at a time, and stores only the recomputed rows.
+    bool redo_any = false;
+#pragma unroll
+    for (int qb = 0; qb < SQB; ++qb) redo_any = redo_any || redo[qb];
+    const bool any_redo = __builtin_amdgcn_ballot_w64(redo_any) != 0;
+    barrier_lds();
+    if (any_redo) {
+#pragma unroll
+        for (int qb = 0; qb < SQB; ++qb) {
+            m_run[qb] = -INFINITY;
+            mc[qb] = -INFINITY;
+            l_part[qb] = 0.0f;
+#pragma unroll
+            for (int db = 0; db < 2; ++db) acc[qb][db] = zero16;
+        }
+        const uint32_t st = lds_addr(smem) + (uint32_t)wave * SSTAGE;
+        for (int j = w_first; j < n_mine; ++j) {
+            const uint32_t base = (uint32_t)j * tile_gbytes;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = lane + 64 * u, r = c >> 3, cc = c & 7;
+                load_lds16(krsrc, st + 1024u * u, base + (uint32_t)r * rsb + 16 * (cc ^ k_swz(r)));
+                load_lds16(vrsrc, st + STILE + 1024u * u,
+                           base + (uint32_t)r * rsb + 16 * (cc ^ v_swz(r)));
+            }
+            wait_vmcnt<0>();
+            f32x16 S[SQB];
+            bf16x8 ka[4], vt[2][2], P[SQB][2];
+            read_k(wave, ka);
+#pragma unroll
+            for (int qb = 0; qb < SQB; ++qb) {
+                S[qb] = mfma32(ka[0], qop[qb][0], zero16);
+#pragma unroll
+                for (int kk = 1; kk < 4; ++kk) S[qb] = mfma32(ka[kk], qop[qb][kk], S[qb]);
+            }
+            mask_tile(j, S);
+            float alpha[SQB];
+            move_reference(S, alpha);
+            rescale(alpha);
+#pragma unroll
+            for (int qb = 0; qb < SQB; ++qb) {
+                const float o = m_run[qb] == -INFINITY ? 0.0f : mc[qb];
+                float lt = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][2 * i], scale_log2e, -o));
+                    const float p1 =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][2 * i + 1], scale_log2e, -o));
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    P[qb][i >> 2][2 * (i & 3)] = pp[0];
+                    P[qb][i >> 2][2 * (i & 3) + 1] = pp[1];
+                    lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);
+                }
+                l_part[qb] += lt;
+            }
+            read_vt(wave, vt);
+#pragma unroll
+            for (int qb = 0; qb < SQB; ++qb)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int db = 0; db < 2; ++db)
+                        acc[qb][db] = mfma32(vt[c][db], P[qb][c], acc[qb][db]);
+            // this tile's LDS reads are done before the next tile's loads
+            // overwrite the stage
+            __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+            asm volatile("" ::: "memory");
+        }
+#pragma unroll
+        for (int qb = 0; qb < SQB; ++qb)
+            if (redo[qb]) finish(qb, true);
+    }
+}
+
+template <int QB, bool WIN>
+hipError_t launch_stream(const AttnArgs& a, hipStream_t stream) {
+    const int bm = 32 * QB * SNW;
+    const int n_qtiles = (a.Lq + bm - 1) / bm;
+    const dim3 grid((unsigned)((long)a.B * a.H * n_qtiles));
+    const float sl2e = (float)(1.4426950408889634 / sqrt((double)SD));
+    const bf16* q = (const bf16*)a.q;
+    const bf16* k = (const bf16*)a.k;
+    const bf16* v = (const bf16*)a.v;
+    bf16* o = (bf16*)a.o;
+    switch (a.mask) {
+        case 0:
+            hipLaunchKernelGGL((attn_stream_bf16<QB, false, false, WIN>), grid, dim3(256), 0,
+                               stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
+                               sl2e, a.window);
+            break;
+        case 1:
+            hipLaunchKernelGGL((attn_stream_bf16<QB, true, false, WIN>), grid, dim3(256), 0,
+                               stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
+                               sl2e, a.window);
+            break;
+        case 2:
+            hipLaunchKernelGGL((attn_stream_bf16<QB, false, true, WIN>), grid, dim3(256), 0,
+                               stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
+                               sl2e, a.window);
+            break;
+        default:
+            hipLaunchKernelGGL((attn_stream_bf16<QB, true, true, WIN>), grid, dim3(256), 0,
+                               stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
+                               sl2e, a.window);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#ifndef STREAM_QB
+#define STREAM_QB 2
+#endif
+
+hipError_t launch_attention_stream_bf16(const AttnArgs& a, hipStream_t stream) {
+    return a.window >= 0 ? launch_stream<STREAM_QB, true>(a, stream)
+                         : launch_stream<STREAM_QB, false>(a, stream);
+}
+
+}  // namespace mha

@@ -19,6 +19,9 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+// The streaming kernel for d = 64 (attn_stream.hip): any row length,
+// restricted attention included.
+hipError_t launch_attention_stream_bf16(const AttnArgs& a, hipStream_t stream);
 
 // Self-attention of every (batch row, head) with the projections fused in:
 // x [B, L, DM], w_q/w_k/w_v [DM, H*64], o [B, L, H, 64]; L <= 128.

@@ -41,6 +41,9 @@ def lengths(batch: int, lo: int, hi: int, seed: int) -> torch.Tensor:
 STAIRCASE_LEVELS = ((0.0, 0.0), (0.12, 5.25), (0.25, 11.25), (0.37, 1.25), (0.5, 31.25),
                     (0.62, 36.75), (0.75, 64.5))
 STAIRCASE_AMPS = (0.0, 1.0, 4.0, 8.0)
+# A staircase that climbs far higher: 130 scaled-logit units above its start
+# at amplitude 8 (about 188 base-2 units), with steps of 30, 70 and 30.
+STAIRCASE_HUGE_LEVELS = ((0.0, 0.0), (0.3, 30.0), (0.6, 100.0), (0.8, 130.0))
 
 
 def staircase(q: torch.Tensor, k: torch.Tensor, levels=STAIRCASE_LEVELS,
