@@ -44,10 +44,21 @@ namespace {
 
 constexpr int SD = 64;                 // head size
 constexpr int SKT = 32;                // keys per tile
-constexpr int SNS = 6;                 // LDS ring stages
-constexpr int SNW = 4;                 // waves per workgroup
+#ifndef STREAM_NS
+#define STREAM_NS 6
+#endif
+constexpr int SNS = STREAM_NS;         // LDS ring stages
+#ifndef STREAM_NW
+#define STREAM_NW 4
+#endif
+constexpr int SNW = STREAM_NW;         // waves per workgroup: 4, or 8 (two per SIMD)
+static_assert(SNW == 4 || SNW == 8, "waves per workgroup");
+// Direct tile loads per thread per tile: a K and a V chunk with four
+// waves; with eight, the first four waves load K and the last four V.
+constexpr int SDMA = SNW == 4 ? 2 : 1;
 constexpr int STILE = SKT * SD * 2;    // bytes of one K (or V) tile: 32 rows of 128 bytes
 constexpr int SSTAGE = 2 * STILE;      // K tile, then V tile
+static_assert(SNS >= 4 && SNS % 2 == 0, "ring: two tiles read, two in flight at least");
 constexpr float L_LIMIT = 1.0e30f;    // a finite row sum at most this is not an overflow
 
 // Tiles from a wave's first whose rows set their reference exactly: the
@@ -63,15 +74,16 @@ constexpr int stream_init_tiles() {
 // register budget then allows.
 template <int QB>
 constexpr int stream_occupancy() {
-    return QB == 1 ? 3 : 2;
+    return SNW == 8 ? 1 : (QB == 1 ? 3 : 2);
 }
 
 template <int QB, bool PAD, bool CAUSAL, bool WIN>
-__global__ __launch_bounds__(256, stream_occupancy<QB>()) void attn_stream_bf16(
+__global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
     int n_qtiles, float scale_log2e, int window) {
-    __shared__ __attribute__((aligned(1024))) char smem[SNS * SSTAGE];
+    // the ring; the recomputation after it takes one stage per wave
+    __shared__ __attribute__((aligned(1024))) char smem[(SNS > SNW ? SNS : SNW) * SSTAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -155,18 +167,26 @@ __global__ __launch_bounds__(256, stream_occupancy<QB>()) void attn_stream_bf16(
     const uint32_t kv_bytes = kv_end > 0 ? (uint32_t)(kv_end - 1) * rsb + SD * 2 : 0u;
     const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kp, kv_bytes);
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vp, kv_bytes);
-    const int pr = tid >> 3, pc = tid & 7;
+    const int pr = (tid & 255) >> 3, pc = tid & 7;
     const uint32_t k_dma = (uint32_t)pr * rsb + 16 * (pc ^ k_swz(pr));
     const uint32_t v_dma = (uint32_t)pr * rsb + 16 * (pc ^ v_swz(pr));
     const uint32_t tile_gbytes = (uint32_t)SKT * rsb;
+    // A wave's 1 KB piece of a stage: with eight waves, waves 4-7 land in
+    // the V half (STILE = 4 KB on).
     const uint32_t lds_wave = lds_addr(smem) + 1024 * wave;
     // Tile t (of the workgroup's stream, jr = t - t_first) into stage jr % SNS.
     auto dma = [&](int jr) {
         const int t = t_first + jr;
         const uint32_t base = t < n_tiles ? (uint32_t)t * tile_gbytes : OOB_OFFSET;
         const uint32_t st = lds_wave + (uint32_t)(jr % SNS) * SSTAGE;
-        load_lds16(krsrc, st, base + k_dma);
-        load_lds16(vrsrc, st + STILE, base + v_dma);
+        if (SNW == 4) {
+            load_lds16(krsrc, st, base + k_dma);
+            load_lds16(vrsrc, st + STILE, base + v_dma);
+        } else if (wave < 4) {
+            load_lds16(krsrc, st, base + k_dma);
+        } else {
+            load_lds16(vrsrc, st, base + v_dma);
+        }
     };
 
     // LDS operand offsets inside a stage (same lane patterns as the
@@ -277,15 +297,17 @@ __global__ __launch_bounds__(256, stream_occupancy<QB>()) void attn_stream_bf16(
     // scale and offset (two FMAs), two exponentials, the rounding to a
     // packed bf16 pair in Pcur, the row-sum step -- run in slots n-2 ..
     // n+1, so no instruction waits for the one just before it.  The MFMAs:
-    // the middle half of the slots the scores of tile j+1 (k slice, query
-    // block), late enough for the K rows to have arrived from LDS and early
-    // enough to be done when the next tile's first values are read; the
-    // first and last quarters the PV of tile j-1 from Pprev (16-key chunk 0,
-    // then 1; query block, d block).  The wave's first SNI tiles (`exact`, a
+    // the first half of the slots the PV of tile j-1 from Pprev and the V^T
+    // operands in va (16-key chunk, query block, d block); the second half
+    // the scores of tile j+1 (k slice, query block), by when its K rows have
+    // arrived from LDS.  Between the halves the V^T reads of tile j (for
+    // its PV in the next tile) are issued, so they land before the tile
+    // ends and the barrier does not wait for them.  The wave's first SNI tiles (`exact`, a
     // wave-uniform flag) move the reference first.
-    auto tile_step = [&](bool exact, int j, int stage_next, f32x16 (&Scur)[SQB],
+    auto tile_step = [&](bool exact, int j, int stage_cur, f32x16 (&Scur)[SQB],
                          f32x16 (&Snext)[SQB], const bf16x8 (&Pprev)[SQB][2],
-                         bf16x8 (&Pcur)[SQB][2], const bf16x8 (&va)[2][2]) {
+                         bf16x8 (&Pcur)[SQB][2], bf16x8 (&va)[2][2]) {
+        const int stage_next = (stage_cur + 1) % SNS;
         bf16x8 ka[4];
         read_k(stage_next, ka);
         mask_tile(j, Scur);
@@ -332,13 +354,13 @@ __global__ __launch_bounds__(256, stream_occupancy<QB>()) void attn_stream_bf16(
 #pragma unroll
         for (int s = 0; s < NSL + 1; ++s) {
             __builtin_amdgcn_sched_barrier(0);
-            if (s >= 2 * SQB && s < 6 * SQB) {
-                const int m = s - 2 * SQB, kk = m / SQB, qb = m % SQB;
-                Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
-            } else if (s < NSL) {
-                const int pv = s < 2 * SQB ? s : s - 4 * SQB;
-                const int c = pv / (2 * SQB), qb = (pv >> 1) % SQB, db = pv & 1;
+            if (s < 4 * SQB) {
+                const int c = s / (2 * SQB), qb = (s >> 1) % SQB, db = s & 1;
                 acc[qb][db] = mfma32(va[c][db], Pprev[qb][c], acc[qb][db]);
+            } else if (s < NSL) {
+                if (s == 4 * SQB) read_vt(stage_cur, va);  // V^T of tile j, for the next tile
+                const int m = s - 4 * SQB, kk = m / SQB, qb = m % SQB;
+                Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
             }
             step_fma(s + 2);
             step_exp(s + 1);
@@ -401,10 +423,11 @@ __global__ __launch_bounds__(256, stream_occupancy<QB>()) void attn_stream_bf16(
     // score and weight register sets alternate with the tile's parity.
     auto iteration = [&](int jr, f32x16 (&Scur)[SQB], f32x16 (&Snext)[SQB],
                          const bf16x8 (&Pprev)[SQB][2], bf16x8 (&Pcur)[SQB][2], int stage) {
-        wait_vmcnt<2 * (SNS - 4)>();
+        wait_vmcnt<SDMA * (SNS - 4)>();
         barrier_lds();
         dma(jr + SNS - 2);
         const int j = t_first + jr;
+        const bool active = j >= w_first && j < n_mine;
         if (j == w_first && j < n_mine) {
             // the wave's first tile: its scores straight from the ring
             bf16x8 ka[4];
@@ -416,18 +439,18 @@ __global__ __launch_bounds__(256, stream_occupancy<QB>()) void attn_stream_bf16(
                 for (int kk = 1; kk < 4; ++kk) Scur[qb] = mfma32(ka[kk], qop[qb][kk], Scur[qb]);
             }
         }
-        if (j >= w_first && j < n_mine) {
-            tile_step(j < w_first + SNI, j, (stage + 1) % SNS, Scur, Snext, Pprev, Pcur, va);
-            read_vt(stage, va);  // V^T of tile j, for its PV in the next tile
+        if (active) {
+            tile_step(j < w_first + SNI, j, stage, Scur, Snext, Pprev, Pcur, va);
         }
     };
+    // Unrolled over the ring (SNS is even, so the register sets alternate
+    // in step): stage u of copy u is a constant.
     for (int jr = 0; jr < n_loop; jr += SNS) {
-        iteration(jr, SA, SB, PB, PA, 0);
-        if (jr + 1 < n_loop) iteration(jr + 1, SB, SA, PA, PB, 1);
-        if (jr + 2 < n_loop) iteration(jr + 2, SA, SB, PB, PA, 2);
-        if (jr + 3 < n_loop) iteration(jr + 3, SB, SA, PA, PB, 3);
-        if (jr + 4 < n_loop) iteration(jr + 4, SA, SB, PB, PA, 4);
-        if (jr + 5 < n_loop) iteration(jr + 5, SB, SA, PA, PB, 5);
+#pragma unroll
+        for (int u = 0; u < SNS; u += 2) {
+            if (jr + u < n_loop) iteration(jr + u, SA, SB, PB, PA, u);
+            if (jr + u + 1 < n_loop) iteration(jr + u + 1, SB, SA, PA, PB, u + 1);
+        }
     }
     // Drain: the PV of the wave's last tile (zero weights if it had none),
     // whose weights sit in the set of that tile's parity.
@@ -561,6 +584,7 @@ __global__ __launch_bounds__(256, stream_occupancy<QB>()) void attn_stream_bf16(
 template <int QB, bool WIN>
 hipError_t launch_stream(const AttnArgs& a, hipStream_t stream) {
     const int bm = 32 * QB * SNW;
+    const dim3 block(64 * SNW);
     const int n_qtiles = (a.Lq + bm - 1) / bm;
     const dim3 grid((unsigned)((long)a.B * a.H * n_qtiles));
     const float sl2e = (float)(1.4426950408889634 / sqrt((double)SD));
@@ -570,22 +594,22 @@ hipError_t launch_stream(const AttnArgs& a, hipStream_t stream) {
     bf16* o = (bf16*)a.o;
     switch (a.mask) {
         case 0:
-            hipLaunchKernelGGL((attn_stream_bf16<QB, false, false, WIN>), grid, dim3(256), 0,
+            hipLaunchKernelGGL((attn_stream_bf16<QB, false, false, WIN>), grid, block, 0,
                                stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
                                sl2e, a.window);
             break;
         case 1:
-            hipLaunchKernelGGL((attn_stream_bf16<QB, true, false, WIN>), grid, dim3(256), 0,
+            hipLaunchKernelGGL((attn_stream_bf16<QB, true, false, WIN>), grid, block, 0,
                                stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
                                sl2e, a.window);
             break;
         case 2:
-            hipLaunchKernelGGL((attn_stream_bf16<QB, false, true, WIN>), grid, dim3(256), 0,
+            hipLaunchKernelGGL((attn_stream_bf16<QB, false, true, WIN>), grid, block, 0,
                                stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
                                sl2e, a.window);
             break;
         default:
-            hipLaunchKernelGGL((attn_stream_bf16<QB, true, true, WIN>), grid, dim3(256), 0,
+            hipLaunchKernelGGL((attn_stream_bf16<QB, true, true, WIN>), grid, block, 0,
                                stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
                                sl2e, a.window);
             break;
