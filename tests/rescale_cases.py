@@ -51,6 +51,13 @@ class Case:
                 f"mask={self.mask}{w} {self.dtype}{hg}")
 
 
+def tiles_name(name: str, mask: int, Lq: int) -> str:
+    """The streaming kernel's query tile for a d = 64 shape without a
+    window: 128 queries for causal rows up to 2048, 256 otherwise."""
+    q = 128 if (mask & CAUSAL) and Lq <= 2048 else 256
+    return f"{name}, {q}-query tiles"
+
+
 def _cases():
     out = []
     for m in (NONE, PAD, CAUSAL, PAD | CAUSAL):
@@ -59,9 +66,10 @@ def _cases():
         # at most 256 keys: eight tiles
         out.append(Case("short rows NT=8", 3, 2, 256 if m & CAUSAL else 200, 256, 64, m))
     for m in (NONE, CAUSAL, PAD | CAUSAL):
-        # the streaming kernel (rows above 256 keys)
-        out.append(Case("long rows", 2, 2, 700, 700, 64, m))
-    out.append(Case("long rows causal", 1, 2, 2200, 2200, 64, CAUSAL))
+        # the streaming kernel (rows above 256 keys): 256-query workgroups
+        # without a mask, 128-query ones for causal rows up to 2048
+        out.append(Case(tiles_name("long rows", m, 700), 2, 2, 700, 700, 64, m))
+    out.append(Case(tiles_name("long rows causal", CAUSAL, 2200), 1, 2, 2200, 2200, 64, CAUSAL))
     out.append(Case("long rows, many heads", 2, 80, 768, 768, 64, NONE, sampled=True))
     out.append(Case("long rows, many heads, padded", 2, 80, 768, 768, 64, PAD, sampled=True))
     for d in (16, 32, 128):
@@ -81,8 +89,9 @@ def _huge_cases():
     reference fixed there would overflow."""
     out = []
     for m in (NONE, PAD, CAUSAL, PAD | CAUSAL):
-        out.append(Case("long rows", 2, 2, 700, 700, 64, m, huge=True))
-    out.append(Case("long rows causal", 1, 2, 2200, 2200, 64, CAUSAL, huge=True))
+        out.append(Case(tiles_name("long rows", m, 700), 2, 2, 700, 700, 64, m, huge=True))
+    out.append(Case(tiles_name("long rows causal", CAUSAL, 2200), 1, 2, 2200, 2200, 64, CAUSAL,
+                    huge=True))
     for m in (NONE, CAUSAL):
         out.append(Case("restricted attention", 2, 2, 1024, 1024, 64, m, window=300, huge=True))
     for d in (16, 32, 128):

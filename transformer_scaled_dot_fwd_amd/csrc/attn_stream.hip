@@ -26,13 +26,14 @@
 // offset, the exponential, the rounding and the row-sum step per value,
 // which with the MFMAs is the work this kernel is bound by at d = 64.
 //
-// Workgroup = 4 waves = one (batch row, head, block of 256 queries); wave w
-// owns 64 queries (two blocks of 32, one query per lane column).  K/V tiles
-// of 32 rows reach LDS by direct global-to-LDS loads into a 6-stage ring,
-// issued four tiles ahead, one barrier per tile.  Per tile j a wave issues
+// Workgroup = 4 waves = one (batch row, head, block of 256 or 128 queries);
+// wave w owns QB blocks of 32 queries (QB = 2 or 1, one query per lane
+// column).  K/V tiles of 32 rows reach LDS by direct global-to-LDS loads
+// into a 6-stage ring, issued four tiles ahead, one barrier per tile.  Per
+// tile j a wave issues
 //
-//   O^T += V_{j-1}^T P_{j-1}^T   8 MFMAs (the previous tile's weights)
-//   S_{j+1}^T = K_{j+1} Q^T      8 MFMAs (the next tile's scores)
+//   O^T += V_{j-1}^T P_{j-1}^T   4 QB MFMAs (the previous tile's weights)
+//   S_{j+1}^T = K_{j+1} Q^T      4 QB MFMAs (the next tile's scores)
 //
 // one per slot, each beside one step of the softmax of S_j, so the matrix
 // core runs while the VALU does the softmax.
@@ -465,55 +466,68 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
             for (int db = 0; db < 2; ++db) acc[qb][db] = mfma32(va[c][db], pl, acc[qb][db]);
         }
 
+    // Every wave is done with the ring (its loads landed, its reads
+    // retired): from here on each wave has its own stage to itself.
+    barrier_lds();
+
     // ---- epilogue: O = acc / l, or 0 for a row with no legal key.  A row
     // whose sum or outputs are not finite (or whose sum exceeds L_LIMIT) is
-    // not stored here but recomputed below; the two lanes holding a row
-    // decide together.  Each store is an 8-byte piece of a query's row, 32
-    // rows per instruction; plain stores let L2 merge a row's pieces into
-    // whole lines.
-    auto finish = [&](int qb, bool store_ok) -> bool {
+    // not stored here but recomputed below; `bad` has bit l (and l + 32) set
+    // for such a row l of the block, the two lanes holding it decide
+    // together.  The 32 x 64 block goes through the wave's stage (chunks
+    // swizzled by row) so that each store writes eight whole 128-byte rows:
+    // a lane holds a query's column, a store wants its row.  The first pass
+    // (again = false) stores the good rows and returns `bad`; the second
+    // stores the rows `first_bad` marks.  Called with every lane active.
+    char* const stg = smem + wave * SSTAGE;
+    auto finish = [&](int qb, bool again, uint64_t first_bad) -> uint64_t {
         const float l_tot = sum_halves(l_part[qb]);
         const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-        bf16x4 out[2][4];
         bool ok = l_tot <= L_LIMIT;  // false for inf and NaN
+        char* const blk = stg + 4096 * qb;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg)
+            for (int rg = 0; rg < 4; ++rg) {
+                bf16x4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float x = acc[qb][db][4 * rg + e] * inv;
                     ok = ok && __builtin_fabsf(x) <= 3.0e38f;
-                    out[db][rg][e] = (bf16)x;
+                    out[e] = (bf16)x;
                 }
+                // d = 32db + 8rg + 4half .. +3: chunk 4db + rg, half of it
+                *(bf16x4*)(blk + l32 * 128 + 16 * ((4 * db + rg) ^ (l32 & 7)) + 8 * half) = out;
+            }
         const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
-        const bool redo = ((bad >> lane) | (bad >> (lane ^ 32))) & 1;
-        const int qi = wq0 + 32 * qb + l32;
-        if (qi < Lq && (store_ok || !redo)) {
-            bf16* orow = op + (size_t)qi * rs;
+        const uint64_t marked = again ? first_bad : bad;
+        const int cc = lane & 7;
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg)
-                    *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * half) = out[db][rg];
+        for (int k = 0; k < 4; ++k) {
+            const int r = (lane >> 3) + 8 * k;
+            const bf16x8 row = *(const bf16x8*)(blk + r * 128 + 16 * (cc ^ (r & 7)));
+            const int qi = wq0 + 32 * qb + r;
+            const bool r_marked = ((marked >> r) | (marked >> (r + 32))) & 1;
+            if (qi < Lq && r_marked == again) *(bf16x8*)(op + (size_t)qi * rs + 8 * cc) = row;
         }
-        return redo;
+        return bad;
     };
-    bool redo[SQB];
+    uint64_t redo[SQB];
 #pragma unroll
-    for (int qb = 0; qb < SQB; ++qb) redo[qb] = finish(qb, false);
+    for (int qb = 0; qb < SQB; ++qb) redo[qb] = finish(qb, false, 0);
 
     // ---- recomputation of the rows that overflowed (rare: a key more than
     // ~88 scaled-logit units above the row's first tiles), with a reference
     // that moves every tile.  The wave streams its tiles alone through its
-    // own stage of the ring (the barrier: every wave is done with the ring),
-    // one tile at a time, and stores only the recomputed rows.
-    bool redo_any = false;
+    // own stage, one tile at a time, and stores only the recomputed rows
+    // (the block's staged reads above are retired: their rows were stored).
+    bool any_redo = false;
 #pragma unroll
-    for (int qb = 0; qb < SQB; ++qb) redo_any = redo_any || redo[qb];
-    const bool any_redo = __builtin_amdgcn_ballot_w64(redo_any) != 0;
-    barrier_lds();
+    for (int qb = 0; qb < SQB; ++qb) any_redo = any_redo || redo[qb] != 0;
     if (any_redo) {
+        // the staged reads retire before loads into the stage are issued
+        __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int qb = 0; qb < SQB; ++qb) {
             m_run[qb] = -INFINITY;
@@ -577,7 +591,7 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
         }
 #pragma unroll
         for (int qb = 0; qb < SQB; ++qb)
-            if (redo[qb]) finish(qb, true);
+            if (redo[qb] != 0) finish(qb, true, redo[qb]);
     }
 }
 
@@ -619,13 +633,17 @@ hipError_t launch_stream(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-#ifndef STREAM_QB
-#define STREAM_QB 2
-#endif
-
+// Workgroups of 128 queries (one block of 32 per wave, three workgroups per
+// CU) where work per workgroup is short or uneven: restricted attention,
+// whose workgroup streams its queries' span plus the window, so a narrower
+// span wastes fewer keys; and causal rows up to 2048 queries, where the
+// spread of workgroup lengths and the diagonal tiles some waves sit out
+// weigh most.  Workgroups of 256 queries otherwise.
 hipError_t launch_attention_stream_bf16(const AttnArgs& a, hipStream_t stream) {
-    return a.window >= 0 ? launch_stream<STREAM_QB, true>(a, stream)
-                         : launch_stream<STREAM_QB, false>(a, stream);
+    if (a.window >= 0) return launch_stream<1, true>(a, stream);
+    const bool causal = (a.mask & 2) != 0;
+    return causal && a.Lq <= 2048 ? launch_stream<1, false>(a, stream)
+                                  : launch_stream<2, false>(a, stream);
 }
 
 }  // namespace mha
