@@ -94,8 +94,10 @@ def _huge_cases():
                     huge=True))
     for m in (NONE, CAUSAL):
         out.append(Case("restricted attention", 2, 2, 1024, 1024, 64, m, window=300, huge=True))
+    out.append(Case("restricted attention", 2, 2, 1024, 1024, 128, NONE, window=300, huge=True))
     for d in (16, 32, 128):
         out.append(Case(f"head size {d}", 2, 2, 600, 600, d, CAUSAL, huge=True))
+    out.append(Case("head size 128", 2, 2, 600, 600, 128, PAD, huge=True))
     return out
 
 

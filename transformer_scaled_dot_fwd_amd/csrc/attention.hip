@@ -869,20 +869,19 @@ hipError_t launch_short_bf16(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     // d = 64: rows of at most 128 (256) keys hold the whole K/V row in LDS
     // at once; longer rows and restricted attention stream through the
-    // kernel of attn_stream.hip.  Other head sizes run this file's
-    // streaming kernel at every length, 32 queries per wave.
+    // kernel of attn_stream.hip, as d = 128 does at every length.  d = 16
+    // and 32 run this file's streaming kernel, 32 queries per wave.
     if (a.window >= 0) {  // restricted attention: the streaming kernels' band variants
         switch (a.D) {
             case 16: return launch_bf16<16, ATTN_NW, 1, true>(a, stream);
             case 32: return launch_bf16<32, ATTN_NW, 1, true>(a, stream);
-            case 128: return launch_bf16<128, 8, 1, true>(a, stream);
             default: return launch_attention_stream_bf16(a, stream);
         }
     }
     switch (a.D) {
         case 16: return launch_bf16<16, ATTN_NW, 1>(a, stream);
         case 32: return launch_bf16<32, ATTN_NW, 1>(a, stream);
-        case 128: return launch_bf16<128, 8, 1>(a, stream);
+        case 128: return launch_attention_stream_bf16(a, stream);
         default: break;
     }
     if (a.Lk <= 128) return launch_short_bf16<4>(a, stream);

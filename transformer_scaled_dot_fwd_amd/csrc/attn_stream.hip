@@ -43,24 +43,24 @@
 namespace mha {
 namespace {
 
-constexpr int SD = 64;                 // head size
 constexpr int SKT = 32;                // keys per tile
-#ifndef STREAM_NS
-#define STREAM_NS 6
-#endif
-constexpr int SNS = STREAM_NS;         // LDS ring stages
-#ifndef STREAM_NW
-#define STREAM_NW 4
-#endif
-constexpr int SNW = STREAM_NW;         // waves per workgroup: 4, or 8 (two per SIMD)
-static_assert(SNW == 4 || SNW == 8, "waves per workgroup");
-// Direct tile loads per thread per tile: a K and a V chunk with four
-// waves; with eight, the first four waves load K and the last four V.
-constexpr int SDMA = SNW == 4 ? 2 : 1;
-constexpr int STILE = SKT * SD * 2;    // bytes of one K (or V) tile: 32 rows of 128 bytes
-constexpr int SSTAGE = 2 * STILE;      // K tile, then V tile
-static_assert(SNS >= 4 && SNS % 2 == 0, "ring: two tiles read, two in flight at least");
+constexpr int SNW = 4;                 // waves per workgroup
 constexpr float L_LIMIT = 1.0e30f;    // a finite row sum at most this is not an overflow
+
+// Sizes that follow from the head size D (64 or 128).
+template <int D>
+struct StreamDims {
+    static constexpr int TILE = SKT * D * 2;      // bytes of one K (or V) tile
+    static constexpr int STAGE = 2 * TILE;        // K tile, then V tile
+    static constexpr int NS = D == 64 ? 6 : 4;    // ring stages (two workgroups' worth per CU)
+    static constexpr int CPR = D / 8;             // 16-byte chunks per row
+    static constexpr int KK = D / 16;             // k slices of a score MFMA
+    static constexpr int DB = D / 32;             // 32-wide d blocks of a PV MFMA
+    static constexpr int LPT = TILE / (64 * SNW * 16);  // direct loads per thread per K (or V) tile
+    static constexpr int DMA = 2 * LPT;           // ... per K and V tile
+    static_assert(NS >= 4 && NS % 2 == 0, "ring: two tiles read, two in flight at least");
+    static_assert(D == 64 || D == 128, "head size");
+};
 
 // Tiles from a wave's first whose rows set their reference exactly: the
 // first tile holds every row's first legal key (key 0), except under
@@ -73,16 +73,26 @@ constexpr int stream_init_tiles() {
 
 // Query blocks of 32 per wave (QB = 1 or 2) and the workgroups per CU the
 // register budget then allows.
-template <int QB>
+template <int D, int QB>
 constexpr int stream_occupancy() {
-    return SNW == 8 ? 1 : (QB == 1 ? 3 : 2);
+    return (D == 64 && QB == 1) ? 3 : 2;
 }
 
-template <int QB, bool PAD, bool CAUSAL, bool WIN>
-__global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_bf16(
+template <int D, int QB, bool PAD, bool CAUSAL, bool WIN>
+__global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_stream_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
     int n_qtiles, float scale_log2e, int window) {
+    using Dm = StreamDims<D>;
+    constexpr int SD = D;
+    constexpr int SNS = Dm::NS;
+    constexpr int STILE = Dm::TILE;
+    constexpr int SSTAGE = Dm::STAGE;
+    constexpr int SDMA = Dm::DMA;
+    constexpr int CPR = Dm::CPR;
+    constexpr int KK = Dm::KK;
+    constexpr int DB = Dm::DB;
+    constexpr int ROWB = CPR * 16;  // bytes of a K, V or O row in LDS
     // the ring; the recomputation after it takes one stage per wave
     __shared__ __attribute__((aligned(1024))) char smem[(SNS > SNW ? SNS : SNW) * SSTAGE];
 
@@ -102,7 +112,11 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
     constexpr int SQB = QB;                // 32-query blocks per wave
     constexpr int SWQ = 32 * SQB;          // queries per wave
     constexpr int SBM = SWQ * SNW;         // queries per workgroup
-    constexpr int NSL = 8 * SQB;           // slots (and MFMAs) per tile
+    constexpr int NPV = 2 * DB * SQB;      // PV MFMAs per tile (two 16-key chunks)
+    constexpr int NSL = NPV + KK * SQB;    // slots (and MFMAs) per tile
+    constexpr int NPR = 8 * SQB;           // pairs of scores per lane per tile
+    constexpr int RAT = NSL / NPR;         // slots per pair: 1 (d = 64) or 2 (d = 128)
+    static_assert(NSL == RAT * NPR && (RAT == 1 || RAT == 2), "slots per pair");
     constexpr int SNI = stream_init_tiles<WIN>();
     const int nbh = B * H;
     const int w = (int)blockIdx.x;
@@ -160,71 +174,75 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
     const bf16* vp = v + ((size_t)b * Lk * H + hh) * SD;
     bf16* op = o + ((size_t)b * Lq * H + hh) * SD;
 
-    bf16x8 qop[SQB][4];  // Q as the B operand of S^T = K Q^T (loaded in the prologue)
+    bf16x8 qop[SQB][KK];  // Q as the B operand of S^T = K Q^T (loaded in the prologue)
 
-    // Direct global-to-LDS tile loads: thread tid fills chunk position tid
-    // of a tile (row tid / 8), fetching the chunk the swizzle puts there;
-    // rows at or past kv_end land as zeros without a memory access.
+    // Direct global-to-LDS tile loads: thread tid fills chunk positions
+    // tid + 256u of a tile (row position / CPR), fetching the chunk the
+    // swizzle puts there; rows at or past kv_end land as zeros without a
+    // memory access.
     const uint32_t kv_bytes = kv_end > 0 ? (uint32_t)(kv_end - 1) * rsb + SD * 2 : 0u;
     const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kp, kv_bytes);
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vp, kv_bytes);
-    const int pr = (tid & 255) >> 3, pc = tid & 7;
-    const uint32_t k_dma = (uint32_t)pr * rsb + 16 * (pc ^ k_swz(pr));
-    const uint32_t v_dma = (uint32_t)pr * rsb + 16 * (pc ^ v_swz(pr));
+    uint32_t k_dma[Dm::LPT], v_dma[Dm::LPT];
+#pragma unroll
+    for (int u = 0; u < Dm::LPT; ++u) {
+        const int pos = tid + 256 * u, pr = pos / CPR, pc = pos % CPR;
+        k_dma[u] = (uint32_t)pr * rsb + 16 * (pc ^ k_swz(pr));
+        v_dma[u] = (uint32_t)pr * rsb + 16 * (pc ^ v_swz(pr));
+    }
     const uint32_t tile_gbytes = (uint32_t)SKT * rsb;
-    // A wave's 1 KB piece of a stage: with eight waves, waves 4-7 land in
-    // the V half (STILE = 4 KB on).
+    // A wave's 1 KB piece of each 4 KB of a stage.
     const uint32_t lds_wave = lds_addr(smem) + 1024 * wave;
-    // Tile t (of the workgroup's stream, jr = t - t_first) into stage jr % SNS.
-    auto dma = [&](int jr) {
+    // Tile t (of the workgroup's stream, jr = t - t_first) into `stage`
+    // (jr % SNS).
+    auto dma = [&](int jr, int stage) {
         const int t = t_first + jr;
         const uint32_t base = t < n_tiles ? (uint32_t)t * tile_gbytes : OOB_OFFSET;
-        const uint32_t st = lds_wave + (uint32_t)(jr % SNS) * SSTAGE;
-        if (SNW == 4) {
-            load_lds16(krsrc, st, base + k_dma);
-            load_lds16(vrsrc, st + STILE, base + v_dma);
-        } else if (wave < 4) {
-            load_lds16(krsrc, st, base + k_dma);
-        } else {
-            load_lds16(vrsrc, st, base + v_dma);
+        const uint32_t st = lds_wave + (uint32_t)stage * SSTAGE;
+#pragma unroll
+        for (int u = 0; u < Dm::LPT; ++u) {
+            load_lds16(krsrc, st + 4096u * u, base + k_dma[u]);
+            load_lds16(vrsrc, st + STILE + 4096u * u, base + v_dma[u]);
         }
     };
 
     // LDS operand offsets inside a stage (same lane patterns as the
     // whole-row kernel): K rows for S^T, V^T by transpose reads.
+    // (Chunks 8 and on of a d = 128 row sit 128 bytes after chunks 0 .. 7,
+    // the swizzle permuting only within each group of eight.)
     uint32_t k_rd[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = l32 * 128 + 16 * ((2 * kk + half) ^ k_swz(l32));
-    uint32_t v_rd[2];
+    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = l32 * ROWB + 16 * ((2 * kk + half) ^ k_swz(l32));
+    uint32_t v_rd[DB];
     {
         const int row = 4 * half + (i16 >> 2);
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < DB; ++db) {
             const int chunk = 4 * db + 2 * (g & 1) + ((i16 & 3) >> 1);
-            v_rd[db] = STILE + row * 128 + 16 * (chunk ^ v_swz(row)) + 8 * (i16 & 1);
+            v_rd[db] = STILE + row * ROWB + 16 * (chunk ^ v_swz(row)) + 8 * (i16 & 1);
         }
     }
-    auto read_k = [&](int stage, bf16x8 (&ka)[4]) {
+    auto read_k = [&](int stage, bf16x8 (&ka)[KK]) {
         const char* base = smem + stage * SSTAGE;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[kk] = *(const bf16x8*)(base + k_rd[kk]);
+        for (int kk = 0; kk < KK; ++kk) ka[kk] = *(const bf16x8*)(base + k_rd[kk & 3] + 128 * (kk >> 2));
     };
     // V^T operands [16-key chunk][d block] of the tile in `stage`.
-    auto read_vt = [&](int stage, bf16x8 (&va)[2][2]) {
+    auto read_vt = [&](int stage, bf16x8 (&va)[2][DB]) {
         const char* base = smem + stage * SSTAGE;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
-                va[c][db] = join(lds_read_tr((const bf16*)(base + 2048 * c + v_rd[db])),
-                                 lds_read_tr((const bf16*)(base + 2048 * c + v_rd[db] + 1024)));
+            for (int db = 0; db < DB; ++db)
+                va[c][db] = join(lds_read_tr((const bf16*)(base + 16 * ROWB * c + v_rd[db])),
+                                 lds_read_tr((const bf16*)(base + 16 * ROWB * c + v_rd[db] + 8 * ROWB)));
     };
 
-    f32x16 acc[SQB][2];
+    f32x16 acc[SQB][DB];
 #pragma unroll
     for (int qb = 0; qb < SQB; ++qb)
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
     // Per query row (this lane's column): the reference m (raw logit units),
@@ -284,32 +302,33 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
 #pragma unroll
         for (int qb = 0; qb < SQB; ++qb) {
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha[qb];
             l_part[qb] *= alpha[qb];
         }
     };
 
-    // One tile j of the pipeline: 8 slots per query block, each issuing one
-    // MFMA and one step of the softmax for four pairs of S_j's values at
-    // once.  Pair n is values 2(n%8), 2(n%8)+1 of query block n/8; its four
-    // steps --
+    // One tile j of the pipeline: NSL slots, each issuing one MFMA, and
+    // beside them the softmax of S_j, a pair of values at a time.  Pair n
+    // is values 2(n%8), 2(n%8)+1 of query block n/8; its four steps --
     // scale and offset (two FMAs), two exponentials, the rounding to a
-    // packed bf16 pair in Pcur, the row-sum step -- run in slots n-2 ..
-    // n+1, so no instruction waits for the one just before it.  The MFMAs:
-    // the first half of the slots the PV of tile j-1 from Pprev and the V^T
-    // operands in va (16-key chunk, query block, d block); the second half
-    // the scores of tile j+1 (k slice, query block), by when its K rows have
-    // arrived from LDS.  Between the halves the V^T reads of tile j (for
-    // its PV in the next tile) are issued, so they land before the tile
-    // ends and the barrier does not wait for them.  The wave's first SNI tiles (`exact`, a
+    // packed bf16 pair in Pcur, the row-sum step -- run one slot apart
+    // (slots n-2 .. n+1 at d = 64, one pair per slot) or two apart (slots
+    // 2n-3 .. 2n at d = 128, where a tile has twice the MFMAs), so no
+    // instruction waits for the one just before it.  The MFMAs: the first
+    // NPV slots the PV of tile j-1 from Pprev and the V^T operands in va
+    // (16-key chunk, query block, d block); the rest the scores of tile
+    // j+1 (k slice, query block), by when its K rows have arrived from
+    // LDS.  Between the two the V^T reads of tile j (for its PV in the next
+    // tile) are issued, so they land before the tile ends and the barrier
+    // does not wait for them.  The wave's first SNI tiles (`exact`, a
     // wave-uniform flag) move the reference first.
     auto tile_step = [&](bool exact, int j, int stage_cur, f32x16 (&Scur)[SQB],
                          f32x16 (&Snext)[SQB], const bf16x8 (&Pprev)[SQB][2],
-                         bf16x8 (&Pcur)[SQB][2], bf16x8 (&va)[2][2]) {
+                         bf16x8 (&Pcur)[SQB][2], bf16x8 (&va)[2][DB]) {
         const int stage_next = (stage_cur + 1) % SNS;
-        bf16x8 ka[4];
+        bf16x8 ka[KK];
         read_k(stage_next, ka);
         mask_tile(j, Scur);
         float alpha[SQB], off[SQB];
@@ -322,51 +341,62 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
         for (int qb = 0; qb < SQB; ++qb)
             off[qb] = (exact && m_run[qb] == -INFINITY) ? 0.0f : mc[qb];
         float lt[SQB];
-        float xs[NSL][2], ex[NSL][2];
-        bf16x2 pk[NSL];
+        float xs[NPR][2], ex[NPR][2];
+        bf16x2 pk[NPR];
         auto step_fma = [&](int n) {
-            if (n < 0 || n >= NSL) return;
+            if (n < 0 || n >= NPR) return;
             const int qb = n >> 3, i = n & 7;
             xs[n][0] = __builtin_fmaf(Scur[qb][2 * i], scale_log2e, -off[qb]);
             xs[n][1] = __builtin_fmaf(Scur[qb][2 * i + 1], scale_log2e, -off[qb]);
         };
         auto step_exp = [&](int n) {
-            if (n < 0 || n >= NSL) return;
+            if (n < 0 || n >= NPR) return;
             ex[n][0] = __builtin_amdgcn_exp2f(xs[n][0]);
             ex[n][1] = __builtin_amdgcn_exp2f(xs[n][1]);
         };
         auto step_round = [&](int n) {
-            if (n < 0 || n >= NSL) return;
+            if (n < 0 || n >= NPR) return;
             const int qb = n >> 3, i = n & 7;
             pk[n] = bf16x2{(bf16)ex[n][0], (bf16)ex[n][1]};
             Pcur[qb][i >> 2][2 * (i & 3)] = pk[n][0];
             Pcur[qb][i >> 2][2 * (i & 3) + 1] = pk[n][1];
         };
         auto step_sum = [&](int n) {
-            if (n < 0 || n >= NSL) return;
+            if (n < 0 || n >= NPR) return;
             const int qb = n >> 3, i = n & 7;
             lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk[n], ones, i == 0 ? 0.0f : lt[qb], false);
         };
-        step_fma(0);
-        step_fma(1);
-        step_exp(0);
+        // The softmax steps beside slot s (negative: before the first MFMA).
+        auto slot_steps = [&](int s) {
+            if (RAT == 1) {
+                step_fma(s + 2);
+                step_exp(s + 1);
+                step_round(s);
+                step_sum(s - 1);
+            } else if ((s & 1) != 0) {
+                step_fma((s + 3) / 2);
+                step_round((s + 1) / 2);
+            } else {
+                step_exp((s + 2) / 2);
+                step_sum(s / 2);
+            }
+        };
+#pragma unroll
+        for (int s = -RAT - 1; s < 0; ++s) slot_steps(s);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int s = 0; s < NSL + 1; ++s) {
+        for (int s = 0; s < NSL + (RAT == 1 ? 1 : 0); ++s) {
             __builtin_amdgcn_sched_barrier(0);
-            if (s < 4 * SQB) {
-                const int c = s / (2 * SQB), qb = (s >> 1) % SQB, db = s & 1;
+            if (s < NPV) {
+                const int c = s / (DB * SQB), qb = (s / DB) % SQB, db = s % DB;
                 acc[qb][db] = mfma32(va[c][db], Pprev[qb][c], acc[qb][db]);
             } else if (s < NSL) {
-                if (s == 4 * SQB) read_vt(stage_cur, va);  // V^T of tile j, for the next tile
-                const int m = s - 4 * SQB, kk = m / SQB, qb = m % SQB;
+                if (s == NPV) read_vt(stage_cur, va);  // V^T of tile j, for the next tile
+                const int m = s - NPV, kk = m / SQB, qb = m % SQB;
                 Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
             }
-            step_fma(s + 2);
-            step_exp(s + 1);
-            step_round(s);
-            step_sum(s - 1);
+            slot_steps(s);
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
@@ -381,7 +411,7 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
     // the waits it places for them stay out of the loop, where they would
     // also wait for the tile loads in flight.)
 #pragma unroll
-    for (int jr = 0; jr < SNS - 2; ++jr) dma(jr);
+    for (int jr = 0; jr < SNS - 2; ++jr) dma(jr, jr);
     // Q as the B operand of S^T = K Q^T: block qb, lane holds query
     // wq0 + 32qb + l32, d = 16kk + 8half .. +7.  Rows past Lq read zeros.
     const __amdgpu_buffer_rsrc_t qrsrc =
@@ -391,19 +421,19 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
         const int qi = wq0 + 32 * qb + l32;
         const uint32_t qoff = qi < Lq ? (uint32_t)qi * rsb + 16 * half : OOB_OFFSET;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
+        for (int kk = 0; kk < KK; ++kk) qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
     }
     // Q's values are consumed here, so the compiler's own wait for them
     // (which also covers the tile loads issued before them) lands here.
 #pragma unroll
     for (int qb = 0; qb < SQB; ++qb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(qop[qb][kk]));
+        for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[qb][kk]));
 
     f32x16 SA[SQB], SB[SQB];
     // Weights of alternate tiles (the previous tile's wait for their PV);
     // V^T of tile j-1.
-    bf16x8 PA[SQB][2], PB[SQB][2], va[2][2];
+    bf16x8 PA[SQB][2], PB[SQB][2], va[2][DB];
 #pragma unroll
     for (int qb = 0; qb < SQB; ++qb)
 #pragma unroll
@@ -414,7 +444,7 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) va[c][db] = zero_bf16x8();
+        for (int db = 0; db < DB; ++db) va[c][db] = zero_bf16x8();
 
     // Iteration jr (tile j = t_first + jr, stage jr % SNS): the tiles up to
     // j + 1 have landed (each thread waits for its own loads of them, the
@@ -426,31 +456,32 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
                          const bf16x8 (&Pprev)[SQB][2], bf16x8 (&Pcur)[SQB][2], int stage) {
         wait_vmcnt<SDMA * (SNS - 4)>();
         barrier_lds();
-        dma(jr + SNS - 2);
+        dma(jr + SNS - 2, (stage + SNS - 2) % SNS);
         const int j = t_first + jr;
         const bool active = j >= w_first && j < n_mine;
         if (j == w_first && j < n_mine) {
             // the wave's first tile: its scores straight from the ring
-            bf16x8 ka[4];
+            bf16x8 ka[KK];
             read_k(stage, ka);
 #pragma unroll
             for (int qb = 0; qb < SQB; ++qb) {
                 Scur[qb] = mfma32(ka[0], qop[qb][0], zero16);
 #pragma unroll
-                for (int kk = 1; kk < 4; ++kk) Scur[qb] = mfma32(ka[kk], qop[qb][kk], Scur[qb]);
+                for (int kk = 1; kk < KK; ++kk) Scur[qb] = mfma32(ka[kk], qop[qb][kk], Scur[qb]);
             }
         }
         if (active) {
             tile_step(j < w_first + SNI, j, stage, Scur, Snext, Pprev, Pcur, va);
         }
     };
-    // Unrolled over the ring (SNS is even, so the register sets alternate
-    // in step): stage u of copy u is a constant.
-    for (int jr = 0; jr < n_loop; jr += SNS) {
+    // Unrolled over the ring (twice when SNS is odd, so the register sets
+    // alternate in step): stage u % SNS of copy u is a constant.
+    constexpr int UNR = SNS % 2 == 0 ? SNS : 2 * SNS;
+    for (int jr = 0; jr < n_loop; jr += UNR) {
 #pragma unroll
-        for (int u = 0; u < SNS; u += 2) {
-            if (jr + u < n_loop) iteration(jr + u, SA, SB, PB, PA, u);
-            if (jr + u + 1 < n_loop) iteration(jr + u + 1, SB, SA, PA, PB, u + 1);
+        for (int u = 0; u < UNR; u += 2) {
+            if (jr + u < n_loop) iteration(jr + u, SA, SB, PB, PA, u % SNS);
+            if (jr + u + 1 < n_loop) iteration(jr + u + 1, SB, SA, PA, PB, (u + 1) % SNS);
         }
     }
     // Drain: the PV of the wave's last tile (zero weights if it had none),
@@ -463,7 +494,7 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
         for (int c = 0; c < 2; ++c) {
             const bf16x8 pl = last_odd ? PB[qb][c] : PA[qb][c];
 #pragma unroll
-            for (int db = 0; db < 2; ++db) acc[qb][db] = mfma32(va[c][db], pl, acc[qb][db]);
+            for (int db = 0; db < DB; ++db) acc[qb][db] = mfma32(va[c][db], pl, acc[qb][db]);
         }
 
     // Every wave is done with the ring (its loads landed, its reads
@@ -474,9 +505,10 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
     // whose sum or outputs are not finite (or whose sum exceeds L_LIMIT) is
     // not stored here but recomputed below; `bad` has bit l (and l + 32) set
     // for such a row l of the block, the two lanes holding it decide
-    // together.  The 32 x 64 block goes through the wave's stage (chunks
-    // swizzled by row) so that each store writes eight whole 128-byte rows:
-    // a lane holds a query's column, a store wants its row.  The first pass
+    // together.  The 32 x D block goes through the wave's stage (chunks
+    // swizzled by row within each group of eight) so that each store writes
+    // whole rows (eight of 128 bytes, or four of 256): a lane holds a
+    // query's column, a store wants its row.  The first pass
     // (again = false) stores the good rows and returns `bad`; the second
     // stores the rows `first_bad` marks.  Called with every lane active.
     char* const stg = smem + wave * SSTAGE;
@@ -484,9 +516,9 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
         const float l_tot = sum_halves(l_part[qb]);
         const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
         bool ok = l_tot <= L_LIMIT;  // false for inf and NaN
-        char* const blk = stg + 4096 * qb;
+        char* const blk = stg + 64 * SD * qb;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 bf16x4 out;
@@ -497,15 +529,15 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
                     out[e] = (bf16)x;
                 }
                 // d = 32db + 8rg + 4half .. +3: chunk 4db + rg, half of it
-                *(bf16x4*)(blk + l32 * 128 + 16 * ((4 * db + rg) ^ (l32 & 7)) + 8 * half) = out;
+                *(bf16x4*)(blk + l32 * ROWB + 16 * ((4 * db + rg) ^ (l32 & 7)) + 8 * half) = out;
             }
         const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
         const uint64_t marked = again ? first_bad : bad;
-        const int cc = lane & 7;
+        const int cc = lane % CPR;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = (lane >> 3) + 8 * k;
-            const bf16x8 row = *(const bf16x8*)(blk + r * 128 + 16 * (cc ^ (r & 7)));
+        for (int k = 0; k < CPR / 2; ++k) {
+            const int r = lane / CPR + (64 / CPR) * k;
+            const bf16x8 row = *(const bf16x8*)(blk + r * ROWB + 16 * (cc ^ (r & 7)));
             const int qi = wq0 + 32 * qb + r;
             const bool r_marked = ((marked >> r) | (marked >> (r + 32))) & 1;
             if (qi < Lq && r_marked == again) *(bf16x8*)(op + (size_t)qi * rs + 8 * cc) = row;
@@ -534,27 +566,27 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
             mc[qb] = -INFINITY;
             l_part[qb] = 0.0f;
 #pragma unroll
-            for (int db = 0; db < 2; ++db) acc[qb][db] = zero16;
+            for (int db = 0; db < DB; ++db) acc[qb][db] = zero16;
         }
         const uint32_t st = lds_addr(smem) + (uint32_t)wave * SSTAGE;
         for (int j = w_first; j < n_mine; ++j) {
             const uint32_t base = (uint32_t)j * tile_gbytes;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = lane + 64 * u, r = c >> 3, cc = c & 7;
+            for (int u = 0; u < STILE / 1024; ++u) {
+                const int c = lane + 64 * u, r = c / CPR, cc = c % CPR;
                 load_lds16(krsrc, st + 1024u * u, base + (uint32_t)r * rsb + 16 * (cc ^ k_swz(r)));
                 load_lds16(vrsrc, st + STILE + 1024u * u,
                            base + (uint32_t)r * rsb + 16 * (cc ^ v_swz(r)));
             }
             wait_vmcnt<0>();
             f32x16 S[SQB];
-            bf16x8 ka[4], vt[2][2], P[SQB][2];
+            bf16x8 ka[KK], vt[2][DB], P[SQB][2];
             read_k(wave, ka);
 #pragma unroll
             for (int qb = 0; qb < SQB; ++qb) {
                 S[qb] = mfma32(ka[0], qop[qb][0], zero16);
 #pragma unroll
-                for (int kk = 1; kk < 4; ++kk) S[qb] = mfma32(ka[kk], qop[qb][kk], S[qb]);
+                for (int kk = 1; kk < KK; ++kk) S[qb] = mfma32(ka[kk], qop[qb][kk], S[qb]);
             }
             mask_tile(j, S);
             float alpha[SQB];
@@ -582,7 +614,7 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
-                    for (int db = 0; db < 2; ++db)
+                    for (int db = 0; db < DB; ++db)
                         acc[qb][db] = mfma32(vt[c][db], P[qb][c], acc[qb][db]);
             // this tile's LDS reads are done before the next tile's loads
             // overwrite the stage
@@ -595,35 +627,35 @@ __global__ __launch_bounds__(64 * SNW, stream_occupancy<QB>()) void attn_stream_
     }
 }
 
-template <int QB, bool WIN>
+template <int D, int QB, bool WIN>
 hipError_t launch_stream(const AttnArgs& a, hipStream_t stream) {
     const int bm = 32 * QB * SNW;
     const dim3 block(64 * SNW);
     const int n_qtiles = (a.Lq + bm - 1) / bm;
     const dim3 grid((unsigned)((long)a.B * a.H * n_qtiles));
-    const float sl2e = (float)(1.4426950408889634 / sqrt((double)SD));
+    const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
     const bf16* q = (const bf16*)a.q;
     const bf16* k = (const bf16*)a.k;
     const bf16* v = (const bf16*)a.v;
     bf16* o = (bf16*)a.o;
     switch (a.mask) {
         case 0:
-            hipLaunchKernelGGL((attn_stream_bf16<QB, false, false, WIN>), grid, block, 0,
+            hipLaunchKernelGGL((attn_stream_bf16<D, QB, false, false, WIN>), grid, block, 0,
                                stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
                                sl2e, a.window);
             break;
         case 1:
-            hipLaunchKernelGGL((attn_stream_bf16<QB, true, false, WIN>), grid, block, 0,
+            hipLaunchKernelGGL((attn_stream_bf16<D, QB, true, false, WIN>), grid, block, 0,
                                stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
                                sl2e, a.window);
             break;
         case 2:
-            hipLaunchKernelGGL((attn_stream_bf16<QB, false, true, WIN>), grid, block, 0,
+            hipLaunchKernelGGL((attn_stream_bf16<D, QB, false, true, WIN>), grid, block, 0,
                                stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
                                sl2e, a.window);
             break;
         default:
-            hipLaunchKernelGGL((attn_stream_bf16<QB, true, true, WIN>), grid, block, 0,
+            hipLaunchKernelGGL((attn_stream_bf16<D, QB, true, true, WIN>), grid, block, 0,
                                stream, q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles,
                                sl2e, a.window);
             break;
@@ -639,11 +671,16 @@ hipError_t launch_stream(const AttnArgs& a, hipStream_t stream) {
 // span wastes fewer keys; and causal rows up to 2048 queries, where the
 // spread of workgroup lengths and the diagonal tiles some waves sit out
 // weigh most.  Workgroups of 256 queries otherwise.
+// At d = 128 a wave holds one block of 32 queries (two workgroups per CU).
 hipError_t launch_attention_stream_bf16(const AttnArgs& a, hipStream_t stream) {
-    if (a.window >= 0) return launch_stream<1, true>(a, stream);
+    if (a.D == 128)
+        return a.window >= 0 ? launch_stream<128, 1, true>(a, stream)
+                             : launch_stream<128, 1, false>(a, stream);
+    if (a.D != 64) return hipErrorInvalidValue;
+    if (a.window >= 0) return launch_stream<64, 1, true>(a, stream);
     const bool causal = (a.mask & 2) != 0;
-    return causal && a.Lq <= 2048 ? launch_stream<1, false>(a, stream)
-                                  : launch_stream<2, false>(a, stream);
+    return causal && a.Lq <= 2048 ? launch_stream<64, 1, false>(a, stream)
+                                  : launch_stream<64, 2, false>(a, stream);
 }
 
 }  // namespace mha
