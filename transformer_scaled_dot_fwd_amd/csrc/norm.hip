@@ -64,6 +64,7 @@ __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
     __shared__ float2 red[NM_WAVES][NM_BM];
     constexpr int GB_BYTES = 2 * N > 1024 ? 2 * N : 1024;  // gamma, then beta, in LDS
     __shared__ __attribute__((aligned(1024))) char s_gb[2 * GB_BYTES];
+    __shared__ __attribute__((aligned(16))) float s_gbf[2][N];  // the same in fp32
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -126,16 +127,18 @@ __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
     }
 
     // The residual rows, prefetched whole (16 bytes per lane, consecutive
-    // lanes along a row) while the product runs; rows past M read as zeros.
+    // lanes along a row) while the product runs; rows past M read as zeros
+    // (range-checked buffer loads: no branch, so nothing waits for them
+    // before the product's loads are issued).
     constexpr int ROW_CHUNKS = N / 8;                          // 16-byte chunks per row
     constexpr int X_PER_LANE = NM_BM * ROW_CHUNKS / (64 * NM_WAVES);
+    const __amdgpu_buffer_rsrc_t xrr = make_rsrc(
+        xres + (size_t)m0 * N, (uint32_t)((size_t)min(M - m0, NM_BM) * N * 2));
     bf16x8 xres_v[X_PER_LANE];
 #pragma unroll
     for (int it = 0; it < X_PER_LANE; ++it) {
         const int idx = tid + 64 * NM_WAVES * it;
-        const int r = idx / ROW_CHUNKS, c = idx % ROW_CHUNKS;
-        xres_v[it] = m0 + r < M ? *(const bf16x8*)(xres + (size_t)(m0 + r) * N + 8 * c)
-                                : zero_bf16x8();
+        xres_v[it] = buffer_load16(xrr, (uint32_t)(16 * idx));
     }
 
     f32x16 acc[NB];
@@ -199,14 +202,6 @@ __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
     // free once every wave has passed the barrier) to the accumulator
     // layout.
     const int f0 = 32 * NB * wave + 4 * half;
-    bf16x4 gv[NB][4], bv[NB][4];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            gv[nb][rg] = *(const bf16x4*)(s_gb + 2 * (f0 + 32 * nb + 8 * rg));
-            bv[nb][rg] = *(const bf16x4*)(s_gb + GB_BYTES + 2 * (f0 + 32 * nb + 8 * rg));
-        }
     char* so = smem;
     barrier_lds();
 #pragma unroll
@@ -215,14 +210,32 @@ __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
         const int r = idx / ROW_CHUNKS, c = idx % ROW_CHUNKS;
         *(bf16x8*)(so + r * OPITCH + 16 * c) = xres_v[it];
     }
+    // Gain and bias are converted to fp32 once per workgroup (a lane then
+    // reads its features' values, the same for all 32 rows, as float4s).
+    for (int f = tid; f < N; f += 64 * NM_WAVES) {
+        s_gbf[0][f] = (float)((const bf16*)s_gb)[f];
+        s_gbf[1][f] = (float)((const bf16*)(s_gb + GB_BYTES))[f];
+    }
     barrier_lds();
+    // acc += x, one exact dot step per element: x * 1 + x' * 0 + acc.  The
+    // selectors are kept in registers: as an operand constant, bf16 (1, 0)
+    // would be encoded as the inline constant 1.0, which this instruction
+    // reads as the fp32 bit pattern, i.e. as (0, 1).
+    bf16x2 pick_lo = {(bf16)1.0f, (bf16)0.0f}, pick_hi = {(bf16)0.0f, (bf16)1.0f};
+    asm volatile("" : "+v"(pick_lo), "+v"(pick_hi));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const bf16x4 xv = *(const bf16x4*)(so + l32 * OPITCH + 2 * (f0 + 32 * nb + 8 * rg));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[nb][4 * rg + e] += (float)xv[e];
+            for (int e = 0; e < 4; e += 2) {
+                const bf16x2 xp = {xv[e], xv[e + 1]};
+                acc[nb][4 * rg + e] =
+                    __builtin_amdgcn_fdot2_f32_bf16(xp, pick_lo, acc[nb][4 * rg + e], false);
+                acc[nb][4 * rg + e + 1] =
+                    __builtin_amdgcn_fdot2_f32_bf16(xp, pick_hi, acc[nb][4 * rg + e + 1], false);
+            }
         }
     // Row statistics.  Each wave takes the mean and the sum of squared
     // deviations of its 32 NB features of the row (two passes over
@@ -271,12 +284,14 @@ __global__ __launch_bounds__(64 * NM_WAVES, 1) void out_proj_post_norm_bf16(
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
+            const int f = f0 + 32 * nb + 8 * rg;
+            const float4 gf = *(const float4*)&s_gbf[0][f];
+            const float4 bf = *(const float4*)&s_gbf[1][f];
+            const float gg[4] = {gf.x, gf.y, gf.z, gf.w}, bb[4] = {bf.x, bf.y, bf.z, bf.w};
             bf16x4 y;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                y[e] = (bf16)__builtin_fmaf((float)gv[nb][rg][e],
-                                            (acc[nb][4 * rg + e] - mu) * inv,
-                                            (float)bv[nb][rg][e]);
+                y[e] = (bf16)__builtin_fmaf(gg[e], (acc[nb][4 * rg + e] - mu) * inv, bb[e]);
             *(bf16x4*)(so + l32 * OPITCH + 2 * (f0 + 32 * nb + 8 * rg)) = y;
         }
     barrier_lds();
