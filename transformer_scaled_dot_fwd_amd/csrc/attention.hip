@@ -17,438 +17,10 @@
 
 namespace mha {
 
-// ---------------------------------------------------------------------------
-// bf16 MFMA path for the other head shapes of "Paper Deep Reading", section
-// 08, Table 3, rows (A): D in {16, 32, 128} (the template also takes 64; the
-// base shape's d = 64 streams through attn_stream.hip).
-//
-// Workgroup = NW waves = one (batch row, head, tile of 32*QB*NW queries).
-// Wave w owns QB blocks of 32 consecutive queries, one query per lane
-// column.  Key/value tiles of 32 rows pass through a 3-stage LDS ring shared
-// by the waves (one barrier per tile):
-//
-//   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, A = K rows (16-byte LDS
-//                      reads), B = Q (registers, loaded once)
-//   O^T += V^T P^T     A = V^T (LDS transpose reads), B = P (registers)
-//
-// S^T takes D/16 MFMAs per 32 x 32 block and O^T += V^T P^T one MFMA per
-// 16-key chunk and 32-wide d block; for D = 16 the d block is half used (its
-// other 16 rows read whatever the LDS row padding holds and are never
-// stored).  Each A operand (a K or V^T fragment) feeds the wave's QB query
-// blocks.
-// Keeping the query in the lane column makes every per-query quantity (row
-// max, row sum, rescale factor) lane-local, with one exchange between the
-// two half-waves.  The PV contraction runs over keys in the order the S^T
-// accumulator holds them, and the V^T transpose reads fetch V rows in that
-// same order.
-//
-// Software pipeline per wave: the score MFMAs of tile j+1 and the PV MFMAs
-// of tile j are interleaved with the softmax VALU work of tile j (for D =
-// 64, one MFMA per two exponentials).  Global loads run two tiles ahead.
-//
-// WIN: restricted self-attention ("Paper Deep Reading", section 05, the
-// complexity table): query i sees keys i - window .. i + window only.  The
-// workgroup streams just the tiles that overlap its queries' band, each
-// wave computes the tiles that overlap its own, and the band's edges are
-// masked like the other masks.
-// ---------------------------------------------------------------------------
-#ifndef ATTN_QB1_OCC
-#define ATTN_QB1_OCC 3
-#endif
-#ifndef ATTN_NW
-#define ATTN_NW 4
-#endif
-
 namespace {
 
 constexpr int D64 = 64;
 constexpr int KT = 32;             // keys per tile
-constexpr int STAGES = 3;          // LDS ring depth
-
-// Waves per SIMD the long-row kernel is built for.
-template <int D, int QB>
-constexpr int attn_occupancy() {
-    return D > 64 ? 2 : (QB == 1 ? ATTN_QB1_OCC : 2);
-}
-
-template <int D, int NW, int QB, bool PAD, bool CAUSAL, bool WIN>
-__global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_bf16(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    bf16* __restrict__ o, const int32_t* __restrict__ kv_lens, int B, int H, int Lq, int Lk,
-    int n_qtiles, float scale_log2e, int window) {
-    static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head size");
-    constexpr int NKK = D / 16;              // 16-wide k slices of q.k
-    constexpr int DP = D < 32 ? 32 : D;      // d extent the PV blocks cover
-    constexpr int NDB = DP / 32;             // 32-wide d blocks of O
-    constexpr int PITCH = DP + 8;            // LDS row pitch in elements
-    constexpr int TILE = KT * PITCH;         // elements per K (or V) tile in LDS
-    constexpr int WQ = 32 * QB;     // queries per wave
-    constexpr int BM = WQ * NW;     // queries per workgroup
-    constexpr int THREADS = 64 * NW;
-    constexpr int ROW_CHUNKS = D / 8;                  // 16-byte chunks per K (or V) row
-    constexpr int TILE_CHUNKS = KT * ROW_CHUNKS;       // per K (or V) tile
-    // 16-byte chunks of K (and of V) per thread and tile; for small D only
-    // the first TILE_CHUNKS threads load.
-    constexpr int CHUNKS = TILE_CHUNKS >= THREADS ? TILE_CHUNKS / THREADS : 1;
-    static_assert(TILE_CHUNKS < THREADS || TILE_CHUNKS == CHUNKS * THREADS, "tile load split");
-    __shared__ __attribute__((aligned(16))) bf16 sK[STAGES * TILE];
-    __shared__ __attribute__((aligned(16))) bf16 sV[STAGES * TILE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = lane >> 5;
-    const int l32 = lane & 31;
-    const int g = lane >> 4;
-    const int i16 = lane & 15;
-
-    // Tile decode.  Workgroups are dispatched to the 8 XCDs round-robin
-    // (workgroup w runs on XCD w % 8); when B*H divides by 8, XCD x gets the
-    // (batch row, head) pairs x*nbh/8 .. (x+1)*nbh/8 - 1 whole, so every query
-    // tile of a pair shares that XCD's L2 for its K/V.  Causal: within each
-    // XCD the longest query tiles are launched first.
-    const int nbh = B * H;
-    const int w = (int)blockIdx.x;
-    int bh, qt;
-    if ((nbh & 7) == 0) {
-        const int x = w & 7, slot = w >> 3, per = nbh >> 3;
-        if (CAUSAL) {
-            qt = n_qtiles - 1 - slot / per;
-            bh = x * per + slot % per;
-        } else {
-            bh = x * per + slot / n_qtiles;
-            qt = slot % n_qtiles;
-        }
-    } else if (CAUSAL) {
-        qt = n_qtiles - 1 - w / nbh;
-        bh = w % nbh;
-    } else {
-        bh = w / n_qtiles;
-        qt = w % n_qtiles;
-    }
-    const int b = bh / H;
-    const int hh = bh - b * H;
-    const int q0 = qt * BM;
-
-    int kv_end = Lk;
-    if (PAD) kv_end = min(max(kv_lens[b], 0), Lk);
-    int key_end = kv_end;
-    if (CAUSAL) key_end = min(key_end, min(q0 + BM, Lq));
-    // The workgroup streams tiles t_first .. n_tiles - 1 (a band around its
-    // queries when WIN; window < Lk, so no sum below overflows).
-    int t_first = 0;
-    if (WIN) {
-        key_end = min(key_end, q0 + BM + window);
-        t_first = max(q0 - window, 0) / KT;
-    }
-    const int n_tiles = (key_end + KT - 1) / KT;
-    const int n_loop = max(n_tiles - t_first, 0);
-
-    // Tiles this wave computes, w_first .. n_mine - 1: none if it holds no
-    // query row; causal stops at the tile holding the wave's last query; a
-    // band starts and stops a window away from the wave's queries.
-    const int wq0 = q0 + WQ * wave;
-    int n_mine = (wq0 < Lq) ? n_tiles : 0;
-    if (CAUSAL) n_mine = min(n_mine, (wq0 + WQ + KT - 1) / KT);
-    int w_first = 0;
-    if (WIN) {
-        n_mine = min(n_mine, (min(kv_end, wq0 + WQ + window) + KT - 1) / KT);
-        w_first = max(wq0 - window, 0) / KT;
-    }
-
-    const size_t rs = (size_t)H * D;  // elements between consecutive positions
-    const bf16* qp = q + ((size_t)b * Lq * H + hh) * D;
-    const bf16* kp = k + ((size_t)b * Lk * H + hh) * D;
-    const bf16* vp = v + ((size_t)b * Lk * H + hh) * D;
-    bf16* op = o + ((size_t)b * Lq * H + hh) * D;
-
-    // Q as the B operand of S^T = K Q^T: block qb, lane holds query
-    // wq0 + 32qb + l32, d = 16kk + 8half .. +7.  Rows past Lq read as zeros.
-    const __amdgpu_buffer_rsrc_t qrsrc =
-        make_rsrc(qp, (uint32_t)(((size_t)(Lq - 1) * rs + D) * sizeof(bf16)));
-    bf16x8 qop[QB][NKK];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qi = wq0 + 32 * qb + l32;
-        const uint32_t qoff =
-            qi < Lq ? (uint32_t)(((size_t)qi * rs + 8 * half) * sizeof(bf16)) : OOB_OFFSET;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) qop[qb][kk] = buffer_load16(qrsrc, qoff + 32 * kk);
-    }
-
-    f32x16 acc[QB][NDB];  // [query block][d block]
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
-    float m_run[QB], l_part[QB];  // running max of the raw logits q.k; this lane's row-sum share
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_run[qb] = -INFINITY;
-        l_part[qb] = 0.0f;
-    }
-
-    // Cooperative tile load: KT rows x 2D bytes of K and of V, 16 B per
-    // chunk, through buffer resources that end at the last legal key row:
-    // rows at or past kv_end read as zeros and are never fetched from memory.
-    const uint32_t kv_bytes =
-        kv_end > 0 ? (uint32_t)(((size_t)(kv_end - 1) * rs + D) * sizeof(bf16)) : 0u;
-    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kp, kv_bytes);
-    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vp, kv_bytes);
-    const bool loader = TILE_CHUNKS >= THREADS || tid < TILE_CHUNKS;
-    uint32_t voff[CHUNKS];  // this thread's chunk offsets inside a tile (loop invariant)
-#pragma unroll
-    for (int u = 0; u < CHUNKS; ++u) {
-        const int c = tid + THREADS * u;
-        voff[u] = (uint32_t)(((size_t)(c / ROW_CHUNKS) * rs + (c % ROW_CHUNKS) * 8) *
-                             sizeof(bf16));
-    }
-    const uint32_t tile_bytes = (uint32_t)((size_t)KT * rs * sizeof(bf16));
-    // Two register sets: loads run two tiles ahead of the LDS ring.
-    bf16x8 kreg[2][CHUNKS], vreg[2][CHUNKS];
-    // Unconditional (branch-free) tile load; tiles at or past n_tiles read
-    // zeros without touching memory.
-    auto gload = [&](int set, int t) {
-        const uint32_t base = t < n_tiles && loader ? (uint32_t)t * tile_bytes : OOB_OFFSET;
-#pragma unroll
-        for (int u = 0; u < CHUNKS; ++u) {
-            kreg[set][u] = buffer_load16(krsrc, base + voff[u]);
-            vreg[set][u] = buffer_load16(vrsrc, base + voff[u]);
-        }
-    };
-    auto sstore = [&](int set, int stage) {
-        if (!loader) return;
-#pragma unroll
-        for (int u = 0; u < CHUNKS; ++u) {
-            const int c = tid + THREADS * u;
-            const int off = stage * TILE + (c / ROW_CHUNKS) * PITCH + (c % ROW_CHUNKS) * 8;
-            *(bf16x8*)(sK + off) = kreg[set][u];
-            *(bf16x8*)(sV + off) = vreg[set][u];
-        }
-    };
-
-    const f32x16 zero16 = {};
-    // S^T for one tile (prologue only): S[qb] = K Q^T, 32 keys x 32 queries.
-    auto scores = [&](int stage, f32x16 (&S)[QB]) {
-        const bf16* kt = sK + stage * TILE + l32 * PITCH + 8 * half;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const bf16x8 a = *(const bf16x8*)(kt + 16 * kk);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                S[qb] = mfma32(a, qop[qb][kk], kk == 0 ? zero16 : S[qb]);
-        }
-    };
-
-    // Online softmax, step 1: mask tile t (boundary tiles only), take the
-    // row maxima and, when a row's maximum grew by more than 2^8 in exp2
-    // units, rescale that row's partial output and sum.  Between rescales
-    // the exponent offset m_run is a stale maximum, so p = exp2((s - m) c)
-    // stays below 2^8: the ratio acc / l is unaffected (softmax(x) =
-    // softmax(x - c) for any c), and bf16/fp32 have range to spare.
-    auto mask_and_max = [&](int t, f32x16 (&S)[QB]) {
-        const int k0 = t * KT;
-        const bool need_mask = (k0 + KT > kv_end) || (CAUSAL && k0 + KT - 1 > wq0) ||
-                               (WIN && (k0 < wq0 + WQ - 1 - window || k0 + KT - 1 > wq0 + window));
-        if (need_mask) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int qi = wq0 + 32 * qb + l32;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + acc_row(r, half);
-                    bool legal = key < kv_end;
-                    if (CAUSAL) legal = legal && key <= qi;
-                    if (WIN) legal = legal && key >= qi - window && key <= qi + window;
-                    S[qb][r] = legal ? S[qb][r] : -INFINITY;
-                }
-            }
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float mx = S[qb][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[qb][r]);
-            mx = max_halves(mx);
-            // True when m_run = -inf and the tile holds a legal key; false
-            // (NaN compare) while every key so far is masked.
-            const bool grow = (mx - m_run[qb]) * scale_log2e > 8.0f;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? mx : m_run[qb];
-                // m_run = -inf gives alpha = exp2(-inf) = 0: nothing accumulated yet.
-                const float alpha =
-                    grow ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * scale_log2e) : 1.0f;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
-                l_part[qb] *= alpha;
-                m_run[qb] = m_new;
-            }
-        }
-    };
-
-    // Online softmax, step 2, for two values of S[qb]: p = exp2(s c - m c) =
-    // exp((s - m)/sqrt(d)), rounded to bf16 into the P operand; the row sum
-    // accumulates the rounded p, the values PV actually uses.
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-    auto exp_pair = [&](const f32x16 (&S)[QB], const float (&mc)[QB], bf16x8 (&pop)[QB][2],
-                        int qb, int i) {
-        const int e = 2 * i;  // register index in S[qb]; chunk e/8, slot e%8
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][e], scale_log2e, -mc[qb]));
-        const float p1 =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][e + 1], scale_log2e, -mc[qb]));
-        const bf16x2 pp = {(bf16)p0, (bf16)p1};
-        pop[qb][e >> 3][e & 7] = pp[0];
-        pop[qb][e >> 3][(e & 7) + 1] = pp[1];
-        l_part[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part[qb], false);
-    };
-
-    // One tile of the pipeline.  Slot s (0 .. 8*QB-1) exponentiates pair s
-    // (query block s/8, values 2(s%8), 2(s%8)+1) and issues MFMAs
-    // s*NM/NSLOT .. (s+1)*NM/NSLOT - 1 of the tile's NM (one per slot for D =
-    // 64).  The first NKK*QB MFMAs are the scores of tile j+1; the rest are
-    // P_j V_j in (query block, chunk, d block) order, each issued once its P
-    // chunk is complete (chunk (qb, c) is done after pair 8qb + 4c + 3);
-    // those not ready at their slot run after the last slot.  sched_barrier
-    // fences keep the order.
-    // j: the tile; jr = j - t_first: its place in the ring.
-    auto tile_step = [&](int j, int jr, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
-        // LDS operands, issued up front: K of tile j+1, V^T of tile j.  P
-        // chunk c covers keys 16c + {0..3, 8..11} (k = 0..7, lanes < 32) and
-        // 16c + {4..7, 12..15} (k = 8..15, lanes >= 32); the matching V^T
-        // operand: lane group g reads columns 32db + 16(g&1) + j of rows
-        // base + 0..3 and base + 8..11, base = 16c + 4(g>>1).
-        const bf16* kt = sK + ((jr + 1) % STAGES) * TILE + l32 * PITCH + 8 * half;
-        bf16x8 ka[NKK];
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) ka[kk] = *(const bf16x8*)(kt + 16 * kk);
-        const bf16* vt = sV + (jr % STAGES) * TILE;
-        bf16x8 va[2][NDB];  // [chunk][d block]
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int row = 16 * c + 4 * (g >> 1) + (i16 >> 2);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int col = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
-                va[c][db] = join(lds_read_tr(vt + row * PITCH + col),
-                                 lds_read_tr(vt + (row + 8) * PITCH + col));
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        mask_and_max(j, Scur);
-        float mc[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            mc[qb] = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb] * scale_log2e;
-        bf16x8 pop[QB][2];  // P^T operands [query block][16-key chunk]
-
-        // Raised priority while this wave feeds the MFMA pipe, so the
-        // arbiter favours a wave in its MFMA phase over one in its softmax
-        // or load phase.
-        __builtin_amdgcn_s_setprio(1);
-        constexpr int NS = NKK * QB;           // score MFMAs
-        constexpr int NPV = 2 * NDB * QB;      // PV MFMAs
-        constexpr int NM = NS + NPV;
-        constexpr int NSLOT = 8 * QB;
-        // PV MFMA n (0 .. NPV-1): query block, chunk, d block; ready at slot
-        // 8qb + 4c + 4.
-        auto pv_ready = [&](int n, int s) {
-            const int qb = n / (2 * NDB), c = (n / NDB) % 2;
-            return s >= 8 * qb + 4 * c + 4;
-        };
-        auto pv = [&](int n) {
-            const int qb = n / (2 * NDB), c = (n / NDB) % 2, db = n % NDB;
-            acc[qb][db] = mfma32(va[c][db], pop[qb][c], acc[qb][db]);
-        };
-#pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m = s * NM / NSLOT; m < (s + 1) * NM / NSLOT; ++m) {
-                if (m < NS) {
-                    const int qb = m % QB, kk = m / QB;
-                    Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
-                } else if (pv_ready(m - NS, s)) {
-                    pv(m - NS);
-                }
-            }
-            exp_pair(Scur, mc, pop, s / 8, s % 8);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < NSLOT; ++s)
-#pragma unroll
-            for (int m = s * NM / NSLOT; m < (s + 1) * NM / NSLOT; ++m)
-                if (m >= NS && !pv_ready(m - NS, s)) pv(m - NS);
-        __builtin_amdgcn_s_setprio(0);
-    };
-
-    // ---- prologue: the first two tiles into the ring, the next two in
-    // flight ----
-    gload(0, t_first);  // two tiles in flight together: one round trip
-    gload(1, t_first + 1);
-    sstore(0, 0);
-    sstore(1, 1);
-    gload(0, t_first + 2);
-    gload(1, t_first + 3);
-    barrier_lds();
-
-    f32x16 SA[QB], SB[QB];
-    if (!WIN && 0 < n_mine) scores(0, SA);
-
-    // ---- main loop, unrolled by two so the score buffers and the load
-    // register sets alternate ----
-    auto iteration = [&](int jr, int set, f32x16 (&Scur)[QB], f32x16 (&Snext)[QB]) {
-        barrier_lds();  // tile jr+1 is stored; everyone is done with tile jr-1
-        sstore(set, (jr + 2) % STAGES);
-        gload(set, t_first + jr + 4);
-        const int j = t_first + jr;
-        // A band that starts after the workgroup's first tile: the wave's
-        // first scores come straight from the ring.
-        if (WIN && j == w_first && j < n_mine) scores(jr % STAGES, Scur);
-        // Past a wave's last tile, S_{j+1} reads a zero or unused stage and
-        // is dropped.
-        if (j >= w_first && j < n_mine) tile_step(j, jr, Scur, Snext);
-    };
-    // Both halves always run (an odd tail costs one barrier and loads that
-    // read zeros), so the load/store pattern is the same on every trip.
-    for (int jr = 0; jr < n_loop; jr += 2) {
-        iteration(jr, 0, SA, SB);
-        iteration(jr + 1, 1, SB, SA);
-    }
-
-    // ---- epilogue: O = acc / l, or 0 for a row with no legal key ----
-    // Each store is an 8-byte piece of a query's row, 32 rows per
-    // instruction.  Plain stores let L2 merge a row's pieces into whole
-    // lines; nontemporal stores (as the full-row writers elsewhere use) would
-    // send every piece to memory on its own, which measured 10-27% slower
-    // overall at 1024 keys and 5-9% at 4096.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l_tot = sum_halves(l_part[qb]);
-        const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-        const int qi = wq0 + 32 * qb + l32;
-        if (qi < Lq) {
-            bf16* orow = op + (size_t)qi * rs;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int col = 32 * db + 8 * rg + 4 * half;
-                    if (D >= 32 || col < D) {
-                        bf16x4 out;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[qb][db][4 * rg + e] * inv);
-                        *(bf16x4*)(orow + col) = out;
-                    }
-                }
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // bf16, d = 64, rows of at most 256 keys (8 tiles): every K/V row of the
@@ -458,9 +30,11 @@ __global__ __launch_bounds__(NW * 64, (attn_occupancy<D, QB>())) void attn_fwd_b
 // owns 32 consecutive queries, one per lane column.  All K/V tiles go to
 // LDS by direct global-to-LDS loads issued together (one memory round trip)
 // behind a single barrier; each wave then runs its tiles with no further
-// synchronisation: S^T = K Q^T (4 MFMAs), mask, online softmax as above,
-// O^T += V^T P^T (4 MFMAs).  The output block is staged through LDS so that
-// each 128-byte (query, head) row is written whole.
+// synchronisation: S^T = K Q^T (4 MFMAs), mask, online softmax (a running
+// row maximum, the partial output rescaled only when the maximum grows by
+// more than 2^8, exact because numerator and denominator share the stale
+// maximum), O^T += V^T P^T (4 MFMAs).  The output block is staged through
+// LDS so that each 128-byte (query, head) row is written whole.
 //
 // LDS tiles here are 32 rows of 128 bytes without padding (a direct load
 // writes 16 contiguous bytes per lane); the eight 16-byte chunks of a row
@@ -561,7 +135,8 @@ __global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
     wait_vmcnt<0>();
     barrier_lds();
 
-    // LDS operand reads (same lane patterns as the long-row kernel).
+    // LDS operand reads (the lane patterns of the streaming kernel in
+    // attn_stream.hip).
     uint32_t k_rd[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) k_rd[kk] = l32 * 128 + 16 * ((2 * kk + half) ^ k_swz(l32));
@@ -612,7 +187,8 @@ __global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
             for (int r = 0; r < 16; ++r) S[r] = acc_row(r, 0) < lim ? S[r] : -INFINITY;
         }
 
-        // Running maximum with the lazy rescale of the long-row kernel.
+        // Running maximum with the lazy rescale (a row moves to a new
+        // maximum only when it exceeds the old one by more than 2^8).
         float mx = S[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
@@ -798,42 +374,6 @@ hipError_t launch_f32_d(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int NW, int QB, bool WIN = false>
-hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
-    constexpr int BM = 32 * QB * NW;
-    const int n_qtiles = (a.Lq + BM - 1) / BM;
-    const dim3 grid((unsigned)((long)a.B * a.H * n_qtiles));
-    const dim3 block(64 * NW);
-    const float sl2e = (float)(1.4426950408889634 / sqrt((double)a.D));
-    const bf16* q = (const bf16*)a.q;
-    const bf16* k = (const bf16*)a.k;
-    const bf16* v = (const bf16*)a.v;
-    bf16* o = (bf16*)a.o;
-    switch (a.mask) {
-        case 0:
-            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, false, false, WIN>), grid, block, 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e,
-                               a.window);
-            break;
-        case 1:
-            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, true, false, WIN>), grid, block, 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e,
-                               a.window);
-            break;
-        case 2:
-            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, false, true, WIN>), grid, block, 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e,
-                               a.window);
-            break;
-        default:
-            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, QB, true, true, WIN>), grid, block, 0, stream,
-                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, sl2e,
-                               a.window);
-            break;
-    }
-    return hipGetLastError();
-}
-
 template <int NT>
 hipError_t launch_short_bf16(const AttnArgs& a, hipStream_t stream) {
     const int n_qtiles = (a.Lq + SHORT_BM - 1) / SHORT_BM;
@@ -869,21 +409,8 @@ hipError_t launch_short_bf16(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
     // d = 64: rows of at most 128 (256) keys hold the whole K/V row in LDS
     // at once; longer rows and restricted attention stream through the
-    // kernel of attn_stream.hip, as d = 128 does at every length.  d = 16
-    // and 32 run this file's streaming kernel, 32 queries per wave.
-    if (a.window >= 0) {  // restricted attention: the streaming kernels' band variants
-        switch (a.D) {
-            case 16: return launch_bf16<16, ATTN_NW, 1, true>(a, stream);
-            case 32: return launch_bf16<32, ATTN_NW, 1, true>(a, stream);
-            default: return launch_attention_stream_bf16(a, stream);
-        }
-    }
-    switch (a.D) {
-        case 16: return launch_bf16<16, ATTN_NW, 1>(a, stream);
-        case 32: return launch_bf16<32, ATTN_NW, 1>(a, stream);
-        case 128: return launch_attention_stream_bf16(a, stream);
-        default: break;
-    }
+    // kernel of attn_stream.hip, as the other head sizes do at every length.
+    if (a.window >= 0 || a.D != 64) return launch_attention_stream_bf16(a, stream);
     if (a.Lk <= 128) return launch_short_bf16<4>(a, stream);
     if (a.Lk <= 256) return launch_short_bf16<8>(a, stream);
     return launch_attention_stream_bf16(a, stream);

@@ -47,19 +47,29 @@ constexpr int SKT = 32;                // keys per tile
 constexpr int SNW = 4;                 // waves per workgroup
 constexpr float L_LIMIT = 1.0e30f;    // a finite row sum at most this is not an overflow
 
-// Sizes that follow from the head size D (64 or 128).
+// Sizes that follow from the head size D (16, 32, 64 or 128).
 template <int D>
 struct StreamDims {
     static constexpr int TILE = SKT * D * 2;      // bytes of one K (or V) tile
-    static constexpr int STAGE = 2 * TILE;        // K tile, then V tile
-    static constexpr int NS = D == 64 ? 6 : 4;    // ring stages (two workgroups' worth per CU)
+    // d = 16: the PV MFMA's 32-wide d block is half used; its upper 16 rows
+    // take V^T rows of ones from a 1 KB block after the V tile, so that
+    // those accumulator rows sum the rounded weights (the row sum l).
+    static constexpr bool LSUM = D == 16;
+    static constexpr int STAGE = 2 * TILE + (LSUM ? 1024 : 0);  // K tile, V tile (, ones)
+    static constexpr int NS = D == 128 ? 4 : 6;   // ring stages
     static constexpr int CPR = D / 8;             // 16-byte chunks per row
+    static constexpr int SWZ = CPR < 8 ? CPR : 8; // chunks permuted together
     static constexpr int KK = D / 16;             // k slices of a score MFMA
-    static constexpr int DB = D / 32;             // 32-wide d blocks of a PV MFMA
-    static constexpr int LPT = TILE / (64 * SNW * 16);  // direct loads per thread per K (or V) tile
-    static constexpr int DMA = 2 * LPT;           // ... per K and V tile
+    static constexpr int DB = D < 32 ? 1 : D / 32;  // 32-wide d blocks of a PV MFMA
+    // Tiles of at least 4 KB: every thread loads LPT chunks of K and of V.
+    // Smaller ones (D = 16, 32): waves 0 and 1 load K, waves 2 and 3 V, as
+    // many as the tile needs, one chunk per thread.
+    static constexpr bool SMALL = TILE < 64 * SNW * 16;
+    static constexpr int LPT = SMALL ? 1 : TILE / (64 * SNW * 16);
+    static constexpr int DMA = SMALL ? 1 : 2 * LPT;  // loads per loading thread per tile
     static_assert(NS >= 4 && NS % 2 == 0, "ring: two tiles read, two in flight at least");
-    static_assert(D == 64 || D == 128, "head size");
+    static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head size");
+    static_assert(!SMALL || TILE <= 2048, "a small tile takes at most two waves");
 };
 
 // Tiles from a wave's first whose rows set their reference exactly: the
@@ -75,7 +85,7 @@ constexpr int stream_init_tiles() {
 // register budget then allows.
 template <int D, int QB>
 constexpr int stream_occupancy() {
-    return (D == 64 && QB == 1) ? 3 : 2;
+    return D <= 32 ? (QB == 1 ? 4 : 3) : (D == 64 && QB == 1) ? 3 : 2;
 }
 
 template <int D, int QB, bool PAD, bool CAUSAL, bool WIN>
@@ -93,6 +103,11 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     constexpr int KK = Dm::KK;
     constexpr int DB = Dm::DB;
     constexpr int ROWB = CPR * 16;  // bytes of a K, V or O row in LDS
+    // Chunk permutations of a row (K rows by row & 7, V rows by
+    // 4 ((row >> 1) & 1) when a row has eight chunks or more; within the
+    // row's chunks otherwise).
+    auto kswz = [](int r) { return r & (Dm::SWZ - 1); };
+    auto vswz = [](int r) { return Dm::SWZ == 8 ? v_swz(r) : 0; };
     // the ring; the recomputation after it takes one stage per wave
     __shared__ __attribute__((aligned(1024))) char smem[(SNS > SNW ? SNS : SNW) * SSTAGE];
 
@@ -113,10 +128,14 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     constexpr int SWQ = 32 * SQB;          // queries per wave
     constexpr int SBM = SWQ * SNW;         // queries per workgroup
     constexpr int NPV = 2 * DB * SQB;      // PV MFMAs per tile (two 16-key chunks)
-    constexpr int NSL = NPV + KK * SQB;    // slots (and MFMAs) per tile
+    constexpr int NSL = NPV + KK * SQB;    // MFMAs per tile
     constexpr int NPR = 8 * SQB;           // pairs of scores per lane per tile
-    constexpr int RAT = NSL / NPR;         // slots per pair: 1 (d = 64) or 2 (d = 128)
-    static_assert(NSL == RAT * NPR && (RAT == 1 || RAT == 2), "slots per pair");
+    // At least one MFMA per pair (d >= 64): a slot per MFMA, RAT slots per
+    // pair (1 at d = 64, 2 at d = 128).  Fewer (d = 16, 32): a slot per
+    // pair, the MFMAs spread over them.
+    constexpr bool DENSE = NSL >= NPR;
+    constexpr int RAT = DENSE ? NSL / NPR : 1;
+    static_assert(!DENSE || (NSL == RAT * NPR && (RAT == 1 || RAT == 2)), "slots per pair");
     constexpr int SNI = stream_init_tiles<WIN>();
     const int nbh = B * H;
     const int w = (int)blockIdx.x;
@@ -184,21 +203,35 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kp, kv_bytes);
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vp, kv_bytes);
     uint32_t k_dma[Dm::LPT], v_dma[Dm::LPT];
+    // Small tiles: this wave's 1 KB piece of the K (waves 0, 1) or V (waves
+    // 2, 3) tile, if the tile has one.
+    const int sub = wave & 1;
+    const bool small_v = wave >= 2;
+    const bool loads = !Dm::SMALL || 1024 * sub < STILE;
 #pragma unroll
     for (int u = 0; u < Dm::LPT; ++u) {
-        const int pos = tid + 256 * u, pr = pos / CPR, pc = pos % CPR;
-        k_dma[u] = (uint32_t)pr * rsb + 16 * (pc ^ k_swz(pr));
-        v_dma[u] = (uint32_t)pr * rsb + 16 * (pc ^ v_swz(pr));
+        const int pos = Dm::SMALL ? 64 * sub + lane : tid + 256 * u;
+        const int pr = pos / CPR, pc = pos % CPR;
+        k_dma[u] = (uint32_t)pr * rsb + 16 * (pc ^ kswz(pr));
+        v_dma[u] = (uint32_t)pr * rsb + 16 * (pc ^ vswz(pr));
     }
     const uint32_t tile_gbytes = (uint32_t)SKT * rsb;
-    // A wave's 1 KB piece of each 4 KB of a stage.
-    const uint32_t lds_wave = lds_addr(smem) + 1024 * wave;
+    // A wave's 1 KB piece of each 4 KB of a stage (small tiles: of its tile).
+    const uint32_t lds_wave = Dm::SMALL ? lds_addr(smem) + (small_v ? STILE : 0) + 1024 * sub
+                                        : lds_addr(smem) + 1024 * wave;
     // Tile t (of the workgroup's stream, jr = t - t_first) into `stage`
     // (jr % SNS).
     auto dma = [&](int jr, int stage) {
         const int t = t_first + jr;
         const uint32_t base = t < n_tiles ? (uint32_t)t * tile_gbytes : OOB_OFFSET;
         const uint32_t st = lds_wave + (uint32_t)stage * SSTAGE;
+        if (Dm::SMALL) {
+            if (loads) {
+                if (small_v) load_lds16(vrsrc, st, base + v_dma[0]);
+                else load_lds16(krsrc, st, base + k_dma[0]);
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < Dm::LPT; ++u) {
             load_lds16(krsrc, st + 4096u * u, base + k_dma[u]);
@@ -212,14 +245,19 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     // the swizzle permuting only within each group of eight.)
     uint32_t k_rd[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = l32 * ROWB + 16 * ((2 * kk + half) ^ k_swz(l32));
+    for (int kk = 0; kk < 4; ++kk)
+        k_rd[kk] = l32 * ROWB + 16 * (((2 * kk + half) & (CPR - 1)) ^ kswz(l32));
     uint32_t v_rd[DB];
     {
         const int row = 4 * half + (i16 >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int chunk = 4 * db + 2 * (g & 1) + ((i16 & 3) >> 1);
-            v_rd[db] = STILE + row * ROWB + 16 * (chunk ^ v_swz(row)) + 8 * (i16 & 1);
+            const int chunk = (4 * db + 2 * (g & 1) + ((i16 & 3) >> 1)) & (CPR - 1);
+            v_rd[db] = STILE + row * ROWB + 16 * (chunk ^ vswz(row)) + 8 * (i16 & 1);
+            // d = 16: lanes 16-31 and 48-63 hold the block's upper rows;
+            // they read the ones (every read of read_vt lands in the block:
+            // offsets below 64, plus at most 512 + 256 + 8)
+            if (Dm::LSUM && (g & 1)) v_rd[db] = 2 * STILE + 8 * (i16 & 7);
         }
     }
     auto read_k = [&](int stage, bf16x8 (&ka)[KK]) {
@@ -362,7 +400,7 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
             Pcur[qb][i >> 2][2 * (i & 3) + 1] = pk[n][1];
         };
         auto step_sum = [&](int n) {
-            if (n < 0 || n >= NPR) return;
+            if (Dm::LSUM || n < 0 || n >= NPR) return;
             const int qb = n >> 3, i = n & 7;
             lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk[n], ones, i == 0 ? 0.0f : lt[qb], false);
         };
@@ -385,15 +423,20 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
         for (int s = -RAT - 1; s < 0; ++s) slot_steps(s);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
+        constexpr int NSLOT = DENSE ? NSL : NPR;  // slots with an MFMA or a pair's step
 #pragma unroll
-        for (int s = 0; s < NSL + (RAT == 1 ? 1 : 0); ++s) {
+        for (int s = 0; s < NSLOT + (RAT == 1 ? 1 : 0); ++s) {
             __builtin_amdgcn_sched_barrier(0);
-            if (s < NPV) {
-                const int c = s / (DB * SQB), qb = (s / DB) % SQB, db = s % DB;
+            // the MFMA of slot s: MFMA s, or (sparse) MFMA m in the first
+            // slot s with s NSL / NPR >= m
+            const int m = DENSE ? (s < NSL ? s : -1)
+                                : (s < NPR && (s * NSL) % NPR < NSL ? (s * NSL) / NPR : -1);
+            if (m >= 0 && m < NPV) {
+                const int c = m / (DB * SQB), qb = (m / DB) % SQB, db = m % DB;
                 acc[qb][db] = mfma32(va[c][db], Pprev[qb][c], acc[qb][db]);
-            } else if (s < NSL) {
-                if (s == NPV) read_vt(stage_cur, va);  // V^T of tile j, for the next tile
-                const int m = s - NPV, kk = m / SQB, qb = m % SQB;
+            } else if (m >= NPV) {
+                if (m == NPV) read_vt(stage_cur, va);  // V^T of tile j, for the next tile
+                const int mm = m - NPV, kk = mm / SQB, qb = mm % SQB;
                 Snext[qb] = mfma32(ka[kk], qop[qb][kk], kk == 0 ? zero16 : Snext[qb]);
             }
             slot_steps(s);
@@ -401,8 +444,10 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (exact) rescale(alpha);  // acc now holds tile j-1's PV
+        if (!Dm::LSUM) {
 #pragma unroll
-        for (int qb = 0; qb < SQB; ++qb) l_part[qb] += lt[qb];
+            for (int qb = 0; qb < SQB; ++qb) l_part[qb] += lt[qb];
+        }
     };
 
     // ---- prologue: tiles 0 .. SNS-3 and Q in flight together, then all
@@ -410,6 +455,13 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     // compiler's wait bookkeeping; with Q's loads retired before the loop,
     // the waits it places for them stay out of the loop, where they would
     // also wait for the tile loads in flight.)
+    if (Dm::LSUM) {  // the ones blocks of every stage (read after the first barrier)
+        const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+        const uint32_t o = __builtin_bit_cast(uint32_t, one2);
+        const uint4 ones4 = {o, o, o, o};
+        for (int i = tid; i < SNS * 64; i += 64 * SNW)
+            *(uint4*)(smem + (i >> 6) * SSTAGE + 2 * STILE + 16 * (i & 63)) = ones4;
+    }
 #pragma unroll
     for (int jr = 0; jr < SNS - 2; ++jr) dma(jr, jr);
     // Q as the B operand of S^T = K Q^T: block qb, lane holds query
@@ -513,7 +565,8 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     // stores the rows `first_bad` marks.  Called with every lane active.
     char* const stg = smem + wave * SSTAGE;
     auto finish = [&](int qb, bool again, uint64_t first_bad) -> uint64_t {
-        const float l_tot = sum_halves(l_part[qb]);
+        // (d = 16: accumulator row 16 + 4 half, element 8, holds l)
+        const float l_tot = Dm::LSUM ? acc[qb][0][8] : sum_halves(l_part[qb]);
         const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
         bool ok = l_tot <= L_LIMIT;  // false for inf and NaN
         char* const blk = stg + 64 * SD * qb;
@@ -521,6 +574,7 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
+                if (4 * db + rg >= CPR) continue;  // d = 16: the block's unused half
                 bf16x4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -529,7 +583,7 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
                     out[e] = (bf16)x;
                 }
                 // d = 32db + 8rg + 4half .. +3: chunk 4db + rg, half of it
-                *(bf16x4*)(blk + l32 * ROWB + 16 * ((4 * db + rg) ^ (l32 & 7)) + 8 * half) = out;
+                *(bf16x4*)(blk + l32 * ROWB + 16 * ((4 * db + rg) ^ kswz(l32)) + 8 * half) = out;
             }
         const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
         const uint64_t marked = again ? first_bad : bad;
@@ -537,7 +591,7 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
 #pragma unroll
         for (int k = 0; k < CPR / 2; ++k) {
             const int r = lane / CPR + (64 / CPR) * k;
-            const bf16x8 row = *(const bf16x8*)(blk + r * ROWB + 16 * (cc ^ (r & 7)));
+            const bf16x8 row = *(const bf16x8*)(blk + r * ROWB + 16 * (cc ^ kswz(r)));
             const int qi = wq0 + 32 * qb + r;
             const bool r_marked = ((marked >> r) | (marked >> (r + 32))) & 1;
             if (qi < Lq && r_marked == again) *(bf16x8*)(op + (size_t)qi * rs + 8 * cc) = row;
@@ -574,9 +628,9 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
 #pragma unroll
             for (int u = 0; u < STILE / 1024; ++u) {
                 const int c = lane + 64 * u, r = c / CPR, cc = c % CPR;
-                load_lds16(krsrc, st + 1024u * u, base + (uint32_t)r * rsb + 16 * (cc ^ k_swz(r)));
+                load_lds16(krsrc, st + 1024u * u, base + (uint32_t)r * rsb + 16 * (cc ^ kswz(r)));
                 load_lds16(vrsrc, st + STILE + 1024u * u,
-                           base + (uint32_t)r * rsb + 16 * (cc ^ v_swz(r)));
+                           base + (uint32_t)r * rsb + 16 * (cc ^ vswz(r)));
             }
             wait_vmcnt<0>();
             f32x16 S[SQB];
@@ -671,12 +725,25 @@ hipError_t launch_stream(const AttnArgs& a, hipStream_t stream) {
 // span wastes fewer keys; and causal rows up to 2048 queries, where the
 // spread of workgroup lengths and the diagonal tiles some waves sit out
 // weigh most.  Workgroups of 256 queries otherwise.
-// At d = 128 a wave holds one block of 32 queries (two workgroups per CU).
+// At d = 128 a wave holds one block of 32 queries (two workgroups per CU);
+// at d = 16 and 32 likewise (four workgroups per CU).
+#ifndef STREAM_QB_SMALL
+#define STREAM_QB_SMALL 1
+#endif
 hipError_t launch_attention_stream_bf16(const AttnArgs& a, hipStream_t stream) {
-    if (a.D == 128)
-        return a.window >= 0 ? launch_stream<128, 1, true>(a, stream)
-                             : launch_stream<128, 1, false>(a, stream);
-    if (a.D != 64) return hipErrorInvalidValue;
+    switch (a.D) {
+        case 16:
+            return a.window >= 0 ? launch_stream<16, 1, true>(a, stream)
+                                 : launch_stream<16, STREAM_QB_SMALL, false>(a, stream);
+        case 32:
+            return a.window >= 0 ? launch_stream<32, 1, true>(a, stream)
+                                 : launch_stream<32, STREAM_QB_SMALL, false>(a, stream);
+        case 128:
+            return a.window >= 0 ? launch_stream<128, 1, true>(a, stream)
+                                 : launch_stream<128, 1, false>(a, stream);
+        case 64: break;
+        default: return hipErrorInvalidValue;
+    }
     if (a.window >= 0) return launch_stream<64, 1, true>(a, stream);
     const bool causal = (a.mask & 2) != 0;
     return causal && a.Lq <= 2048 ? launch_stream<64, 1, false>(a, stream)
