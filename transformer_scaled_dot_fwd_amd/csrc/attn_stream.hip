@@ -1,5 +1,6 @@
 // attn_stream.hip -- streaming scaled dot-product attention forward for
-// gfx950, d = 64, rows longer than the whole-row-in-LDS kernel takes:
+// gfx950: head sizes 16, 32 and 128 at every length, and d = 64 rows longer
+// than the whole-row-in-LDS kernel takes:
 //
 //   O = softmax(Q K^T / sqrt(d_k) + M) V        for every (batch row, head)
 //
@@ -24,19 +25,22 @@
 // per-tile row maximum and no per-tile data-dependent branch (a branch on
 // a VALU compare waits for the wave's MFMAs in flight): only the scale and
 // offset, the exponential, the rounding and the row-sum step per value,
-// which with the MFMAs is the work this kernel is bound by at d = 64.
+// which with the MFMAs is the work this kernel is bound by at d = 64 (at
+// d = 16 and 32 the softmax alone; at d = 16 the row sum is taken by the
+// PV MFMA's otherwise unused half block).
 //
 // Workgroup = 4 waves = one (batch row, head, block of 256 or 128 queries);
 // wave w owns QB blocks of 32 queries (QB = 2 or 1, one query per lane
 // column).  K/V tiles of 32 rows reach LDS by direct global-to-LDS loads
-// into a 6-stage ring, issued four tiles ahead, one barrier per tile.  Per
-// tile j a wave issues
+// into a 6-stage ring (4 at d = 128), issued up to four tiles ahead, one
+// barrier per tile.  Per tile j a wave issues
 //
-//   O^T += V_{j-1}^T P_{j-1}^T   4 QB MFMAs (the previous tile's weights)
-//   S_{j+1}^T = K_{j+1} Q^T      4 QB MFMAs (the next tile's scores)
+//   O^T += V_{j-1}^T P_{j-1}^T   2 QB max(d/32, 1) MFMAs (the previous
+//                                tile's weights)
+//   S_{j+1}^T = K_{j+1} Q^T      QB d/16 MFMAs (the next tile's scores)
 //
-// one per slot, each beside one step of the softmax of S_j, so the matrix
-// core runs while the VALU does the softmax.
+// beside the steps of the softmax of S_j, so the matrix core runs while the
+// VALU does the softmax.
 #include "device.h"
 #include "launch.h"
 
