@@ -48,6 +48,9 @@ namespace mha {
 namespace {
 
 constexpr int SKT = 32;                // keys per tile
+#ifndef STREAM_BAR2
+#define STREAM_BAR2 1
+#endif
 constexpr int SNW = 4;                 // waves per workgroup
 constexpr float L_LIMIT = 1.0e30f;    // a finite row sum at most this is not an overflow
 
@@ -141,6 +144,8 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     constexpr int RAT = DENSE ? NSL / NPR : 1;
     static_assert(!DENSE || (NSL == RAT * NPR && (RAT == 1 || RAT == 2)), "slots per pair");
     constexpr int SNI = stream_init_tiles<WIN>();
+    // a barrier every other tile (six ring stages), else every tile
+    constexpr bool BAR2 = STREAM_BAR2 && Dm::NS >= 6;
     const int nbh = B * H;
     const int w = (int)blockIdx.x;
     int bh, qt;
@@ -502,17 +507,30 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
 #pragma unroll
         for (int db = 0; db < DB; ++db) va[c][db] = zero_bf16x8();
 
-    // Iteration jr (tile j = t_first + jr, stage jr % SNS): the tiles up to
-    // j + 1 have landed (each thread waits for its own loads of them, the
-    // barrier for everyone's) and every wave is done with tile j - 2's
-    // stage, which the load of tile j + SNS - 2 then takes.  The loop body
-    // is unrolled over the ring so every LDS offset is an immediate; the
-    // score and weight register sets alternate with the tile's parity.
+    // Iteration jr (tile j = t_first + jr, stage jr % SNS) reads tile j's
+    // V and tile j + 1's K.  With a 4-stage ring it first waits for tile
+    // j + 1 (each thread for its own loads of it, the barrier for
+    // everyone's), after which every wave is done with tile j - 2's stage,
+    // which the load of tile j + 2 then takes.  With six stages the waves
+    // meet every other tile: at even jr each waits for all of its loads
+    // (tiles up to j + 3, issued two iterations before), and after the
+    // barrier tiles j + 4 and j + 5 go to the stages of tiles j - 2 and
+    // j - 1, which every wave has left; odd iterations neither wait nor
+    // load.  The loop body is unrolled over the ring so every LDS offset is
+    // an immediate (and jr's parity is that of the stage); the score and
+    // weight register sets alternate with the tile's parity.
     auto iteration = [&](int jr, f32x16 (&Scur)[SQB], f32x16 (&Snext)[SQB],
                          const bf16x8 (&Pprev)[SQB][2], bf16x8 (&Pcur)[SQB][2], int stage) {
-        wait_vmcnt<SDMA * (SNS - 4)>();
-        barrier_lds();
-        dma(jr + SNS - 2, (stage + SNS - 2) % SNS);
+        if (!BAR2) {
+            wait_vmcnt<SDMA * (SNS - 4)>();
+            barrier_lds();
+            dma(jr + SNS - 2, (stage + SNS - 2) % SNS);
+        } else if ((stage & 1) == 0) {
+            wait_vmcnt<0>();
+            barrier_lds();
+            dma(jr + SNS - 2, (stage + SNS - 2) % SNS);
+            dma(jr + SNS - 1, (stage + SNS - 1) % SNS);
+        }
         const int j = t_first + jr;
         const bool active = j >= w_first && j < n_mine;
         if (j == w_first && j < n_mine) {
