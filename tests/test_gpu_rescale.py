@@ -139,5 +139,5 @@ def test_rows_climbing_past_the_fp32_range(case):
     torch.cuda.synchronize()
     ref, s = oracle.attention(q, k, v, mask=case.mask, kv_lens=lens, window=case.window,
                               return_s=True)
-    assert (climbs(s, 3 if case.window is not None else 1) > 130).sum() > 0
+    assert (climbs(s, 2 if case.window is not None else 1) > 130).sum() > 0
     check(o, ref, case.dtype, case.label())

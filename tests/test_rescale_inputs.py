@@ -44,13 +44,13 @@ def test_staircase_reaches_the_fused_kernel_exactly():
 @pytest.mark.parametrize("case", HUGE_CASES, ids=lambda c: c.label())
 def test_huge_staircase_climbs_past_the_fp32_range(case):
     """Some rows' maxima rise more than 127 base-2 units above their first
-    tiles (3 under restricted attention), so a reference fixed there would
+    tiles (2 under restricted attention), so a reference fixed there would
     give p = inf; other rows stay below that."""
     q, k, v, lens = inputs(case, 7400)
     sl = (slice(0, 2), slice(None), slice(0, 1))
     _, s = oracle.attention(q[sl], k[sl], v[sl], mask=case.mask,
                             kv_lens=None if lens is None else lens[:2],
                             return_s=True, window=case.window)
-    c = climbs(s, 3 if case.window is not None else 1)
+    c = climbs(s, 2 if case.window is not None else 1)
     assert (c > 130).sum() >= 4, (case.label(), np.sort(c)[-5:])
     assert (c < 120).sum() >= 4, case.label()

@@ -15,8 +15,8 @@
 // row: p = exp2((s - m) log2(e) / sqrt(d)), acc += p v, l += p, and O = acc
 // / l at the end.  This is the exact identity softmax(x) = softmax(x - c)
 // for any c; m only has to keep p inside the fp32/bf16 range.  m is the
-// row maximum over the wave's first tile (its first three under restricted
-// attention, where a row's band may start up to two tiles in), found
+// row maximum over the wave's first tile (its first two under restricted
+// attention, where a row's band may start a tile in), found
 // exactly, and then stays fixed: a later key would have to exceed it by
 // more than ~88 scaled-logit units (2^127 in p) to overflow.  A row whose
 // sum or output is not finite at the end (that overflow, or a row with no
@@ -84,11 +84,11 @@ struct StreamDims {
 
 // Tiles from a wave's first whose rows set their reference exactly: the
 // first tile holds every row's first legal key (key 0), except under
-// restricted attention, where the band of the wave's last row (63 rows on)
-// starts up to two tiles later.
-template <bool WIN>
+// restricted attention, where the band of the wave's last row (31 rows on
+// with one query block, 63 with two) starts up to one (two) tiles later.
+template <bool WIN, int QB>
 constexpr int stream_init_tiles() {
-    return WIN ? 3 : 1;
+    return WIN ? 1 + QB : 1;
 }
 
 // Query blocks of 32 per wave (QB = 1 or 2) and the workgroups per CU the
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     constexpr bool DENSE = NSL >= NPR;
     constexpr int RAT = DENSE ? NSL / NPR : 1;
     static_assert(!DENSE || (NSL == RAT * NPR && (RAT == 1 || RAT == 2)), "slots per pair");
-    constexpr int SNI = stream_init_tiles<WIN>();
+    constexpr int SNI = stream_init_tiles<WIN, SQB>();
     // a barrier every other tile (six ring stages), else every tile
     constexpr bool BAR2 = STREAM_BAR2 && Dm::NS >= 6;
     // The slots raise the wave's priority with two query blocks per wave
