@@ -16,8 +16,8 @@
 // / l at the end.  This is the exact identity softmax(x) = softmax(x - c)
 // for any c; m only has to keep p inside the fp32/bf16 range.  m is the
 // row maximum over the wave's first tile (its first two under restricted
-// attention, where a row's band may start a tile in), found
-// exactly, and then stays fixed: a later key would have to exceed it by
+// attention, where a row's band may start a tile in), found exactly, and
+// then stays fixed: a later key would have to exceed it by
 // more than ~88 scaled-logit units (2^127 in p) to overflow.  A row whose
 // sum or output is not finite at the end (that overflow, or a row with no
 // legal key in its first tiles) is recomputed by the wave with a running
@@ -32,8 +32,9 @@
 // Workgroup = 4 waves = one (batch row, head, block of 256 or 128 queries);
 // wave w owns QB blocks of 32 queries (QB = 2 or 1, one query per lane
 // column).  K/V tiles of 32 rows reach LDS by direct global-to-LDS loads
-// into a 6-stage ring (4 at d = 128), issued up to four tiles ahead, one
-// barrier per tile.  Per tile j a wave issues
+// into a 6-stage ring, two tiles at a time behind a barrier every other
+// tile (at d = 128 a 4-stage ring, a tile at a time behind a barrier per
+// tile).  Per tile j a wave issues
 //
 //   O^T += V_{j-1}^T P_{j-1}^T   2 QB max(d/32, 1) MFMAs (the previous
 //                                tile's weights)
@@ -48,13 +49,16 @@ namespace mha {
 namespace {
 
 constexpr int SKT = 32;                // keys per tile
+constexpr int SNW = 4;                 // waves per workgroup
+// Tuning switches (the defaults are the measured best): a barrier every
+// other tile with a 6-stage ring; the slots' priority raise with one query
+// block per wave.
 #ifndef STREAM_BAR2
 #define STREAM_BAR2 1
 #endif
 #ifndef STREAM_PRIO_QB1
 #define STREAM_PRIO_QB1 0
 #endif
-constexpr int SNW = 4;                 // waves per workgroup
 constexpr float L_LIMIT = 1.0e30f;    // a finite row sum at most this is not an overflow
 
 // Sizes that follow from the head size D (16, 32, 64 or 128).
@@ -113,9 +117,9 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     constexpr int KK = Dm::KK;
     constexpr int DB = Dm::DB;
     constexpr int ROWB = CPR * 16;  // bytes of a K, V or O row in LDS
-    // Chunk permutations of a row (K rows by row & 7, V rows by
-    // 4 ((row >> 1) & 1) when a row has eight chunks or more; within the
-    // row's chunks otherwise).
+    // Chunk permutations of a row: K rows by row & 7 (by row & 1 or row & 3
+    // for rows of 2 or 4 chunks), V rows by 4 ((row >> 1) & 1) for rows of 8
+    // chunks or more and not at all for shorter ones.
     auto kswz = [](int r) { return r & (Dm::SWZ - 1); };
     auto vswz = [](int r) { return Dm::SWZ == 8 ? v_swz(r) : 0; };
     // the ring; the recomputation after it takes one stage per wave
@@ -755,18 +759,16 @@ hipError_t launch_stream(const AttnArgs& a, hipStream_t stream) {
 // spread of workgroup lengths and the diagonal tiles some waves sit out
 // weigh most.  Workgroups of 256 queries otherwise.
 // At d = 128 a wave holds one block of 32 queries (two workgroups per CU);
-// at d = 16 and 32 likewise (four workgroups per CU).
-#ifndef STREAM_QB_SMALL
-#define STREAM_QB_SMALL 1
-#endif
+// at d = 16 and 32 likewise (four workgroups per CU; two blocks per wave ran
+// slower).
 hipError_t launch_attention_stream_bf16(const AttnArgs& a, hipStream_t stream) {
     switch (a.D) {
         case 16:
             return a.window >= 0 ? launch_stream<16, 1, true>(a, stream)
-                                 : launch_stream<16, STREAM_QB_SMALL, false>(a, stream);
+                                 : launch_stream<16, 1, false>(a, stream);
         case 32:
             return a.window >= 0 ? launch_stream<32, 1, true>(a, stream)
-                                 : launch_stream<32, STREAM_QB_SMALL, false>(a, stream);
+                                 : launch_stream<32, 1, false>(a, stream);
         case 128:
             return a.window >= 0 ? launch_stream<128, 1, true>(a, stream)
                                  : launch_stream<128, 1, false>(a, stream);
