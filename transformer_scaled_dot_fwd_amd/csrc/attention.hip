@@ -255,97 +255,192 @@ __global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
 }
 
 // ---------------------------------------------------------------------------
-// fp32, d in {8, 16, 32, 64}: the accuracy path (exact fp32 FMAs, accurate
-// expf).  One wave per (batch row, head, 64 queries), one query per lane;
-// K/V tiles of 64 rows staged in LDS; online softmax one key at a time.
+// fp32, d in {8, 16, 32, 64}: the accuracy path, on the matrix cores
+// (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation), with exact
+// fp32 scaling and accurate expf.
+//
+// Workgroup = 4 waves = one (batch row, head, block of 128 queries); wave w
+// owns 32 consecutive queries, one per lane column.  K/V tiles of 32 rows
+// are staged in LDS as fp32 (rows at or past the length as zeros, so no
+// value stored there can reach the output).  Per tile a wave computes
+//   S^T = K Q^T      D/2 MFMAs: lane (i, h = lane / 32) feeds K[key i][d]
+//                    and Q[query i][d] for d = h D/2 + s at step s
+//   scale, mask, online softmax with a running maximum (the partial output
+//                    rescaled whenever the maximum grows)
+//   O^T += V^T P^T   16 MFMAs per 32-row block of d: step s takes the
+//                    weight of accumulator register s, i.e. key
+//                    (s % 4) + 8 (s / 4) + 4 h, which is the one the lane
+//                    already holds, so P never moves between lanes.
+// For d < 32 the unused rows of the d block read zeros and are not stored.
 // ---------------------------------------------------------------------------
-constexpr int F32_BM = 64;
-constexpr int F32_BN = 64;
+constexpr int F32_BM = 128;  // queries per workgroup
+constexpr int F32_KT = 32;   // keys per tile
 
-template <int D, bool PAD, bool CAUSAL>
-__global__ __launch_bounds__(64) void attn_fwd_f32(const float* __restrict__ q,
-                                                   const float* __restrict__ k,
-                                                   const float* __restrict__ v,
-                                                   float* __restrict__ o,
-                                                   const int32_t* __restrict__ kv_lens, int B,
-                                                   int H, int Lq, int Lk, int n_qtiles,
-                                                   float scale, int window) {
-    __shared__ float sK[F32_BN][D + 1];
-    __shared__ float sV[F32_BN][D + 1];
-    const int lane = threadIdx.x;
+template <int D, bool PAD, bool CAUSAL, bool WIN>
+__global__ __launch_bounds__(256, 2) void attn_mfma_f32(const float* __restrict__ q,
+                                                        const float* __restrict__ k,
+                                                        const float* __restrict__ v,
+                                                        float* __restrict__ o,
+                                                        const int32_t* __restrict__ kv_lens,
+                                                        int B, int H, int Lq, int Lk,
+                                                        int n_qtiles, float scale, int window) {
+    static_assert(D == 8 || D == 16 || D == 32 || D == 64, "head size");
+    constexpr int DH = D / 2;               // d values each half-wave feeds to S^T
+    constexpr int PITCH = D + 4;            // LDS row pitch in floats (rows 16 B apart in bank)
+    constexpr int DB = D < 32 ? 1 : D / 32; // 32-row blocks of O^T
+    constexpr int C4 = D / 4;               // float4 chunks per row
+    __shared__ __attribute__((aligned(16))) float sK[F32_KT * PITCH];
+    __shared__ __attribute__((aligned(16))) float sV[F32_KT * PITCH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;
+    const int i = lane & 31;
     const int bh = (int)(blockIdx.x / n_qtiles);
     const int qt = (int)(blockIdx.x % n_qtiles);
     const int b = bh / H;
     const int hh = bh - b * H;
     const int q0 = qt * F32_BM;
+
     int kv_end = Lk;
     if (PAD) kv_end = min(max(kv_lens[b], 0), Lk);
     int key_end = kv_end;
     if (CAUSAL) key_end = min(key_end, min(q0 + F32_BM, Lq));
-    int k_start = 0;  // restricted attention (window >= 0): the band only
-    if (window >= 0) {
+    int t_first = 0;  // restricted attention: the workgroup's band only
+    if (WIN) {
         key_end = min(key_end, q0 + F32_BM + window);
-        k_start = max(q0 - window, 0) / F32_BN * F32_BN;
+        t_first = max(q0 - window, 0) / F32_KT;
+    }
+    const int n_tiles = (key_end + F32_KT - 1) / F32_KT;
+    // This wave's tiles: none without a query row; causal stops at the tile
+    // of its last query; a band starts and stops a window away.
+    const int wq0 = q0 + 32 * wave;
+    int n_mine = (wq0 < Lq) ? n_tiles : 0;
+    if (CAUSAL) n_mine = min(n_mine, (wq0 + 32 + F32_KT - 1) / F32_KT);
+    int w_first = t_first;
+    if (WIN) {
+        n_mine = min(n_mine, (min(kv_end, wq0 + 32 + window) + F32_KT - 1) / F32_KT);
+        w_first = max(wq0 - window, 0) / F32_KT;
     }
 
     const size_t rs = (size_t)H * D;
     const float* qp = q + ((size_t)b * Lq * H + hh) * D;
     const float* kp = k + ((size_t)b * Lk * H + hh) * D;
     const float* vp = v + ((size_t)b * Lk * H + hh) * D;
-    const int my_q = q0 + lane;
+    float* op = o + ((size_t)b * Lq * H + hh) * D;
 
-    float qv[D], acc[D];
+    // Q as the B operand of S^T: query wq0 + i, d = h DH .. h DH + DH - 1.
+    const int qi = wq0 + i;
+    float qr[DH];
 #pragma unroll
-    for (int c = 0; c < D; ++c) {
-        qv[c] = (my_q < Lq) ? qp[(size_t)my_q * rs + c] : 0.0f;
-        acc[c] = 0.0f;
+    for (int s = 0; s < DH; s += 4) {
+        float4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (qi < Lq) x = *(const float4*)(qp + (size_t)qi * rs + h * DH + s);
+        qr[s] = x.x;
+        qr[s + 1] = x.y;
+        qr[s + 2] = x.z;
+        qr[s + 3] = x.w;
     }
-    float m_run = -INFINITY, l_run = 0.0f;
 
-    for (int k0 = k_start; k0 < key_end; k0 += F32_BN) {
-        __syncthreads();
-        for (int idx = lane; idx < F32_BN * D; idx += 64) {
-            const int row = idx / D, col = idx % D;
-            const int key = k0 + row;
-            const bool in = key < kv_end;
-            sK[row][col] = in ? kp[(size_t)key * rs + col] : 0.0f;
-            sV[row][col] = in ? vp[(size_t)key * rs + col] : 0.0f;
-        }
-        __syncthreads();
-        const int n = min(F32_BN, key_end - k0);
-        for (int j = 0; j < n; ++j) {
-            const int key = k0 + j;
-            if (key >= kv_end) break;
-            if (CAUSAL && key > my_q) break;
-            if (window >= 0 && key > my_q + window) break;
-            if (window >= 0 && key < my_q - window) continue;
-            float dot = 0.0f;
+    f32x16 acc[DB];
 #pragma unroll
-            for (int c = 0; c < D; ++c) dot = __builtin_fmaf(qv[c], sK[j][c], dot);
-            const float s = dot * scale;
-            if (s > m_run) {
-                const float alpha = expf(m_run - s);  // 0 when m_run = -inf
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int c = 0; c < D; ++c) acc[c] *= alpha;
-                l_run *= alpha;
-                m_run = s;
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    float m_run = -INFINITY, l_part = 0.0f;
+
+    for (int t = t_first; t < n_tiles; ++t) {
+        __syncthreads();  // every wave is done with the previous tile
+        for (int idx = tid; idx < F32_KT * C4; idx += 256) {
+            const int row = idx / C4, c = idx % C4;
+            const int key = t * F32_KT + row;
+            float4 kx = {0.0f, 0.0f, 0.0f, 0.0f}, vx = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (key < kv_end) {
+                kx = *(const float4*)(kp + (size_t)key * rs + 4 * c);
+                vx = *(const float4*)(vp + (size_t)key * rs + 4 * c);
             }
-            const float p = expf(s - m_run);
-            l_run += p;
+            *(float4*)(sK + row * PITCH + 4 * c) = kx;
+            *(float4*)(sV + row * PITCH + 4 * c) = vx;
+        }
+        __syncthreads();
+        if (t < w_first || t >= n_mine) continue;  // wave-uniform
+
+        // S^T = K Q^T: lane (i, h) holds key t*32 + (r % 4) + 8 (r / 4) + 4h
+        // of query qi in register r.
+        f32x16 S;
 #pragma unroll
-            for (int c = 0; c < D; ++c) acc[c] = __builtin_fmaf(p, sV[j][c], acc[c]);
+        for (int r = 0; r < 16; ++r) S[r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < DH; s += 4) {
+            const float4 kx = *(const float4*)(sK + i * PITCH + h * DH + s);
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.x, qr[s], S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.y, qr[s + 1], S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.z, qr[s + 2], S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.w, qr[s + 3], S, 0, 0, 0);
+        }
+        // Scale (after the product, as the attention equation orders them),
+        // then -inf at illegal pairs.
+        float x[16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = t * F32_KT + acc_row(r, h);
+            bool legal = key < kv_end;
+            if (CAUSAL) legal = legal && key <= qi;
+            if (WIN) legal = legal && key >= qi - window && key <= qi + window;
+            x[r] = legal ? S[r] * scale : -INFINITY;
+            mx = fmaxf(mx, x[r]);
+        }
+        mx = max_halves(mx);
+        const float m_new = fmaxf(m_run, mx);
+        // No legal key yet (m_new = -inf): weights 0, nothing rescaled.
+        const bool none = m_new == -INFINITY;
+        const float alpha = none ? 1.0f : expf(m_run - m_new);  // 0 while m_run = -inf
+        float p[16];
+        float lt = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = none ? 0.0f : expf(x[r] - m_new);
+            lt += p[r];
+        }
+        l_part = l_part * alpha + lt;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            // O^T[dd][q] += sum over keys of V[key][dd] P[q][key]; lane (i, h)
+            // feeds V[key (s % 4) + 8 (s / 4) + 4h][dd = 32 db + i].
+            const int dd = 32 * db + i;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const float a = dd < D ? sV[acc_row(s, h) * PITCH + dd] : 0.0f;
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[s], acc[db], 0, 0, 0);
+            }
         }
     }
-    if (my_q < Lq) {
-        const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
-        float* orow = o + ((size_t)b * Lq * H + hh) * D + (size_t)my_q * rs;
+
+    // O = acc / l (0 for a row with no legal key).  Lane (i, h) holds
+    // O[qi][32 db + 8 j + 4 h .. + 3] in registers 4 j .. 4 j + 3.
+    const float l_tot = sum_halves(l_part);
+    const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+    if (qi < Lq) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) orow[c] = acc[c] * inv;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 32 * db + 8 * j + 4 * h;
+                if (d0 >= D) continue;
+                const float4 out = {acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv,
+                                    acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv};
+                *(float4*)(op + (size_t)qi * rs + d0) = out;
+            }
     }
 }
 
-template <int D>
-hipError_t launch_f32_d(const AttnArgs& a, hipStream_t stream) {
+template <int D, bool WIN>
+hipError_t launch_f32_dw(const AttnArgs& a, hipStream_t stream) {
     const int n_qtiles = (a.Lq + F32_BM - 1) / F32_BM;
     const dim3 grid((unsigned)((long)a.B * a.H * n_qtiles));
     const float scale = (float)(1.0 / sqrt((double)D));
@@ -355,23 +450,32 @@ hipError_t launch_f32_d(const AttnArgs& a, hipStream_t stream) {
     float* o = (float*)a.o;
     switch (a.mask) {
         case 0:
-            hipLaunchKernelGGL((attn_fwd_f32<D, false, false>), grid, dim3(64), 0, stream, q, k, v,
-                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale, a.window);
+            hipLaunchKernelGGL((attn_mfma_f32<D, false, false, WIN>), grid, dim3(256), 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale,
+                               a.window);
             break;
         case 1:
-            hipLaunchKernelGGL((attn_fwd_f32<D, true, false>), grid, dim3(64), 0, stream, q, k, v,
-                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale, a.window);
+            hipLaunchKernelGGL((attn_mfma_f32<D, true, false, WIN>), grid, dim3(256), 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale,
+                               a.window);
             break;
         case 2:
-            hipLaunchKernelGGL((attn_fwd_f32<D, false, true>), grid, dim3(64), 0, stream, q, k, v,
-                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale, a.window);
+            hipLaunchKernelGGL((attn_mfma_f32<D, false, true, WIN>), grid, dim3(256), 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale,
+                               a.window);
             break;
         default:
-            hipLaunchKernelGGL((attn_fwd_f32<D, true, true>), grid, dim3(64), 0, stream, q, k, v,
-                               o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale, a.window);
+            hipLaunchKernelGGL((attn_mfma_f32<D, true, true, WIN>), grid, dim3(256), 0, stream,
+                               q, k, v, o, a.kv_lens, a.B, a.H, a.Lq, a.Lk, n_qtiles, scale,
+                               a.window);
             break;
     }
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32_d(const AttnArgs& a, hipStream_t stream) {
+    return a.window >= 0 ? launch_f32_dw<D, true>(a, stream) : launch_f32_dw<D, false>(a, stream);
 }
 
 template <int NT>
