@@ -264,55 +264,89 @@ __global__ __launch_bounds__(GT, OCC) void out_projection_gemm(GemmBatch batch, 
 }
 
 // ---------------------------------------------------------------------------
-// fp32 GEMM (accuracy path): 64 x 64 tile, k step 16, each thread 4 x 4
-// outputs with exact fp32 FMAs.
+// fp32 GEMM (accuracy path) on the matrix cores: v_mfma_f32_32x32x2_f32
+// (fp32 operands, fp32 accumulation).  64 x 64 output tile per workgroup,
+// wave (wm, wn) owning the 32 x 32 block at (32 wm, 32 wn); k step 32.
+// At MFMA step s (0..15) lane (i, h = lane / 32) feeds X[m = i][k = 16 h + s]
+// (A, 16-byte LDS reads of consecutive k) and W[k = 16 h + s][n = i] (B).
+// The next k step's tiles are loaded into registers while the MFMAs of this
+// one run, then stored to LDS between two barriers.  Rows past M read as
+// zeros and are not stored.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmBatch batch, int N, int K) {
+constexpr int F32G_BK = 32;
+constexpr int F32G_XP = F32G_BK + 4;  // X tile row pitch (floats): rows 16 B apart in bank
+constexpr int F32G_WP = 64 + 4;       // W tile row pitch (floats)
+
+__global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmBatch batch, int N, int K) {
     const GemmProblem P = batch.p[blockIdx.z];
     const int M = P.M;
     const int m0 = blockIdx.x * 64;
-    if (m0 >= M) return;
+    if (m0 >= M) return;  // uniform across the workgroup, before any barrier
     const int n0 = blockIdx.y * 64;
     const float* X = (const float*)P.x;
     const float* W = (const float*)P.w;
     float* Y = (float*)P.y;
-    __shared__ float sX[64][17];
-    __shared__ float sW[16][65];
+    __shared__ __attribute__((aligned(16))) float sX[64 * F32G_XP];
+    __shared__ __attribute__((aligned(16))) float sW[F32G_BK * F32G_WP];
+
     const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        __syncthreads();
-        for (int u = 0; u < 4; ++u) {
-            const int idx = tid + 256 * u;
-            const int xr = idx >> 4, xc = idx & 15;
-            sX[xr][xc] = (m0 + xr < M) ? X[(size_t)(m0 + xr) * K + k0 + xc] : 0.0f;
-            const int wr = idx >> 6, wc = idx & 63;
-            sW[wr][wc] = (n0 + wc < N) ? W[(size_t)(k0 + wr) * N + n0 + wc] : 0.0f;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = lane & 31;
+    const int h = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Tile loads: X is 64 rows x 8 chunks of 4 floats, W 32 rows x 16 chunks;
+    // thread tid takes chunks tid and tid + 256 of each.
+    float4 xr[2], wr[2];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int cx = tid + 256 * u;
+            const int row = cx >> 3, c = cx & 7;
+            float4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (m0 + row < M) z = *(const float4*)(X + (size_t)(m0 + row) * K + k0 + 4 * c);
+            xr[u] = z;
+            const int cw = tid + 256 * u;
+            const int wrow = cw >> 4, wc = cw & 15;
+            wr[u] = *(const float4*)(W + (size_t)(k0 + wrow) * N + n0 + 4 * wc);
         }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int cx = tid + 256 * u;
+            *(float4*)(sX + (cx >> 3) * F32G_XP + 4 * (cx & 7)) = xr[u];
+            *(float4*)(sW + (cx >> 4) * F32G_WP + 4 * (cx & 15)) = wr[u];
+        }
+    };
+
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    load(0);
+    for (int k0 = 0; k0 < K; k0 += F32G_BK) {
+        __syncthreads();  // every wave is done with the previous tiles
+        store();
         __syncthreads();
+        if (k0 + F32G_BK < K) load(k0 + F32G_BK);
+        const float* xa = sX + (32 * wm + i) * F32G_XP + 16 * h;
+        const float* wb = sW + (16 * h) * F32G_WP + 32 * wn + i;
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = sX[ty * 4 + i][kk];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = sW[kk][tx * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        for (int s = 0; s < 16; s += 4) {
+            const float4 a = *(const float4*)(xa + s);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, wb[s * F32G_WP], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, wb[(s + 1) * F32G_WP], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, wb[(s + 2) * F32G_WP], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, wb[(s + 3) * F32G_WP], acc, 0, 0, 0);
         }
     }
+    // Lane (i, h) holds Y[m0 + 32 wm + acc_row(r, h)][n0 + 32 wn + i] in
+    // register r: each store writes 32 consecutive floats of a row.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + ty * 4 + i;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + tx * 4 + j;
-            if (n < N) Y[(size_t)m * N + n] = acc[i][j];
-        }
+    for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * wm + acc_row(r, h);
+        if (m < M) Y[(size_t)m * N + n0 + 32 * wn + i] = acc[r];
     }
 }
 
