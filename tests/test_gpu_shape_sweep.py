@@ -104,7 +104,10 @@ F32_CASES = [dict(d=d, B=2, h=3, Lq=Lq, Lk=Lk, mask=m, window=w, lens=[Lk, max(L
                   seed=72000 + n)
              for n, (d, Lq, Lk, m, w) in enumerate([(8, 17, 17, CAUSAL, None), (16, 70, 33, PAD, None),
                                                       (32, 130, 130, PAD | CAUSAL, 9),
-                                                      (64, 65, 65, NONE, 20), (64, 100, 190, PAD, None)])]
+                                                      (64, 65, 65, NONE, 20), (64, 100, 190, PAD, None),
+                                                      (64, 300, 300, CAUSAL, None),
+                                                      (16, 257, 257, PAD | CAUSAL, 40),
+                                                      (8, 129, 300, PAD, None)])]
 
 
 @pytest.mark.parametrize("case", F32_CASES, ids=label)
