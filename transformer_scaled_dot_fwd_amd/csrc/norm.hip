@@ -316,15 +316,21 @@ hipError_t launch_post_norm_d(const PostNormArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 (accuracy path): the same computation with exact fp32 FMAs on the
-// VALU.  A workgroup of 256 threads owns 16 whole rows; thread i holds
-// columns i, i + 256, ... (NPT of them) of every row.  O's rows stream
-// through LDS in chunks of 256 k; W^O is read one row of k at a time,
-// coalesced across the threads.  The row statistics are two passes (mean,
-// then squared deviations) reduced over the workgroup through LDS.
+// fp32 (accuracy path): the same computation on the matrix cores
+// (v_mfma_f32_32x32x2_f32: fp32 products and accumulation), for any h*d_v.
+// A workgroup of 4 waves owns 32 whole rows; wave w holds columns
+// w N/4 .. (w+1) N/4 - 1 as N/128 accumulators of 32 x 32 (lane (i, h =
+// lane / 32) holds column i of each block, rows (r % 4) + 8 (r / 4) + 4h).
+// k steps of 8 through LDS: at MFMA step s lane half h feeds k = 4h + s of
+// the step, O[row i][k] (A) and W^O[k][column i] (B); past K both tiles
+// hold zeros.  The next step's tiles are loaded into registers while the
+// MFMAs of this one run.  The row statistics are two passes (mean, then
+// squared deviations), reduced over each half-wave's 32 lanes and then
+// over the four waves through LDS.
 // ---------------------------------------------------------------------------
-constexpr int NF_R = 16;    // rows per workgroup
-constexpr int NF_KC = 256;  // k chunk
+constexpr int NF_R = 32;   // rows per workgroup
+constexpr int NF_KS = 8;   // k step
+constexpr int NF_OP = NF_KS + 4;  // O tile row pitch (floats)
 
 template <int NPT>
 __global__ __launch_bounds__(256) void out_proj_post_norm_f32(
@@ -332,86 +338,125 @@ __global__ __launch_bounds__(256) void out_proj_post_norm_f32(
     const float* __restrict__ gamma, const float* __restrict__ beta, float* out, int M, int K,
     float eps) {
     constexpr int N = 256 * NPT;
-    __shared__ float so[NF_R][NF_KC];
+    constexpr int NB = N / 128;       // 32-column blocks per wave
+    constexpr int WP = N + 4;         // W tile row pitch (floats)
+    constexpr int WC = NF_KS * N / 4 / 256;  // float4 chunks of the W tile per thread
+    __shared__ __attribute__((aligned(16))) float so[NF_R * NF_OP];
+    __shared__ __attribute__((aligned(16))) float sw[NF_KS * WP];
     __shared__ float red[4][NF_R];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = lane & 31;
+    const int h = lane >> 5;
     const int m0 = (int)blockIdx.x * NF_R;
     const int rows = min(NF_R, M - m0);
+    const int c0 = wave * (N / 4);    // this wave's first column
 
-    float acc[NF_R][NPT];
+    // Tile loads of k step k0: thread t takes O[m0 + t / 8][k0 + t % 8] and
+    // the W^O chunks t, t + 256, ... (row c / (N / 4), 4 floats each).
+    float oreg;
+    float4 wreg[WC];
+    auto load = [&](int k0) {
+        const int r = tid >> 3, kk = k0 + (tid & 7);
+        oreg = (r < rows && kk < K) ? o[(size_t)(m0 + r) * K + kk] : 0.0f;
 #pragma unroll
-    for (int r = 0; r < NF_R; ++r)
-#pragma unroll
-        for (int c = 0; c < NPT; ++c) acc[r][c] = 0.0f;
-    for (int k0 = 0; k0 < K; k0 += NF_KC) {
-        const int kc = min(NF_KC, K - k0);
-        __syncthreads();  // the previous chunk is consumed
-        for (int i = tid; i < NF_R * NF_KC; i += 256) {
-            const int r = i / NF_KC, kk = i % NF_KC;
-            so[r][kk] = (r < rows && kk < kc) ? o[(size_t)(m0 + r) * K + k0 + kk] : 0.0f;
+        for (int u = 0; u < WC; ++u) {
+            const int c = tid + 256 * u;
+            const int wr = c / (N / 4), wc = c % (N / 4);
+            float4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (k0 + wr < K) z = *(const float4*)(w + (size_t)(k0 + wr) * N + 4 * wc);
+            wreg[u] = z;
         }
+    };
+    auto store = [&]() {
+        so[(tid >> 3) * NF_OP + (tid & 7)] = oreg;
+#pragma unroll
+        for (int u = 0; u < WC; ++u) {
+            const int c = tid + 256 * u;
+            *(float4*)(sw + (c / (N / 4)) * WP + 4 * (c % (N / 4))) = wreg[u];
+        }
+    };
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+    load(0);
+    for (int k0 = 0; k0 < K; k0 += NF_KS) {
+        __syncthreads();  // every wave is done with the previous tiles
+        store();
         __syncthreads();
-        for (int kk = 0; kk < kc; ++kk) {
-            float wv[NPT];
+        if (k0 + NF_KS < K) load(k0 + NF_KS);
+        const f32x4 a = *(const f32x4*)(so + i * NF_OP + 4 * h);
 #pragma unroll
-            for (int c = 0; c < NPT; ++c) wv[c] = w[(size_t)(k0 + kk) * N + tid + 256 * c];
+        for (int b = 0; b < NB; ++b) {
+            const float* wb = sw + (4 * h) * WP + c0 + 32 * b + i;
 #pragma unroll
-            for (int r = 0; r < NF_R; ++r)
-#pragma unroll
-                for (int c = 0; c < NPT; ++c) acc[r][c] = __builtin_fmaf(so[r][kk], wv[c], acc[r][c]);
+            for (int s = 0; s < 4; ++s)
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], wb[s * WP], acc[b], 0, 0, 0);
         }
     }
-    // residual (rows past M stay zero and are never stored)
-#pragma unroll
-    for (int r = 0; r < NF_R; ++r)
-        if (r < rows)
-#pragma unroll
-            for (int c = 0; c < NPT; ++c) acc[r][c] += xres[(size_t)(m0 + r) * N + tid + 256 * c];
 
-    // Sum of v over each row of the workgroup: lanes, then the four waves.
-    auto row_sums = [&](const float (&v)[NF_R], float (&tot)[NF_R]) {
+    // Residual (rows past M stay zero and are never stored).  Register r of
+    // block b holds row acc_row(r, h), column c0 + 32 b + i.
 #pragma unroll
-        for (int r = 0; r < NF_R; ++r) {
+    for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, h);
+        if (row < rows)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                acc[b][r] += xres[(size_t)(m0 + row) * N + c0 + 32 * b + i];
+    }
+
+    // Sum of v[r] over each row: the 32 lanes of the half-wave, then the
+    // four waves.  tot[r] is the total of row acc_row(r, h).
+    auto row_sums = [&](const float (&v)[16], float (&tot)[16]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
             float x = v[r];
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-            if (lane == 0) red[wave][r] = x;
+            for (int off = 16; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+            if (i == 0) red[wave][acc_row(r, h)] = x;
         }
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < NF_R; ++r) tot[r] = red[0][r] + red[1][r] + red[2][r] + red[3][r];
+        for (int r = 0; r < 16; ++r) {
+            const int row = acc_row(r, h);
+            tot[r] = red[0][row] + red[1][row] + red[2][row] + red[3][row];
+        }
         __syncthreads();
     };
-    float part[NF_R], mu[NF_R], var[NF_R];
+    float part[16], mu[16], var[16];
 #pragma unroll
-    for (int r = 0; r < NF_R; ++r) {
+    for (int r = 0; r < 16; ++r) {
         part[r] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NPT; ++c) part[r] += acc[r][c];
+        for (int b = 0; b < NB; ++b) part[r] += acc[b][r];
     }
     row_sums(part, mu);
 #pragma unroll
-    for (int r = 0; r < NF_R; ++r) {
+    for (int r = 0; r < 16; ++r) {
         mu[r] *= 1.0f / N;
         part[r] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NPT; ++c) {
-            const float dz = acc[r][c] - mu[r];
+        for (int b = 0; b < NB; ++b) {
+            const float dz = acc[b][r] - mu[r];
             part[r] = __builtin_fmaf(dz, dz, part[r]);
         }
     }
     row_sums(part, var);
 #pragma unroll
-    for (int r = 0; r < NF_R; ++r) {
-        if (r >= rows) continue;
+    for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, h);
+        if (row >= rows) continue;
         const float inv = 1.0f / sqrtf(var[r] * (1.0f / N) + eps);
 #pragma unroll
-        for (int c = 0; c < NPT; ++c) {
-            const int col = tid + 256 * c;
-            out[(size_t)(m0 + r) * N + col] =
-                __builtin_fmaf(gamma[col], (acc[r][c] - mu[r]) * inv, beta[col]);
+        for (int b = 0; b < NB; ++b) {
+            const int col = c0 + 32 * b + i;
+            out[(size_t)(m0 + row) * N + col] =
+                __builtin_fmaf(gamma[col], (acc[b][r] - mu[r]) * inv, beta[col]);
         }
     }
 }
