@@ -50,6 +50,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+PEAK_FP32_FLOPS = 157.3e12    # MI355X dense fp32 (vector and matrix)
 ROTATE_BYTES = 1 << 30        # rotate buffers over >= 1 GiB (Infinity Cache is 256 MB)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
@@ -785,6 +786,65 @@ def block_step(dev, args, copy_gbps):
     return out
 
 
+def fp32_path(dev, steps, warmup):
+    """The fp32 (accuracy) path, which runs on the matrix cores too: the tiny
+    workload (c1, launch-bound) and fp32 inputs at the base shapes --
+    attention at h = 8, d = 64, L = 1024, B = 4 without a mask, and the base
+    block's projections, W^O and post-norm (X [64, 128, 512]).  Rotating
+    input sets, direct launches, median of five timed regions."""
+    import torch
+    import transformer_scaled_dot_fwd_amd as mha
+    from workloads import configs, generate
+    out = []
+
+    def entry(name, what, fn, sets, flops):
+        sec = time_median(fn, sets, max(warmup, len(sets)), None,
+                          min_calls=max(steps // 4, 2 * len(sets)))
+        tf = flops / sec / 1e12
+        out.append({"kernel": name, "what": what, "us": round(sec * 1e6, 2),
+                    "tflops": round(tf, 2), "frac_peak_fp32": round(tf * 1e12 / PEAK_FP32_FLOPS, 4)})
+        log(f"  fp32 {name}: {sec * 1e6:.1f} us, {tf:.2f} TFLOP/s")
+
+    w = configs.get("c1")
+    inp = configs.make_inputs(w)
+    sets = [{k: v.to(dev) for k, v in inp.items() if v is not None} for _ in range(4)]
+    entry("attention", w.description,
+          lambda s: mha.mha_forward(s["q"], s["k"], s["v"]), sets,
+          4.0 * w.d * w.B * w.h * w.Lq * w.Lk)
+    B, L, h, d = 4, 1024, 8, 64
+    sets = [{"q": generate.normal((B, L, h, d), 9600 + 3 * i, "f32").to(dev),
+             "k": generate.normal((B, L, h, d), 9601 + 3 * i, "f32").to(dev),
+             "v": generate.normal((B, L, h, d), 9602 + 3 * i, "f32").to(dev)} for i in range(4)]
+    for s in sets:
+        s["o"] = torch.empty_like(s["q"])
+    entry("attention", f"B={B} h={h} L={L} d={d} fp32, no mask",
+          lambda s: mha.mha_forward(s["q"], s["k"], s["v"], out=s["o"]), sets,
+          4.0 * d * B * h * L * L)
+    del sets
+    B, L, dm, h = 64, 128, 512, 8
+    M = B * L
+    sets = []
+    for i in range(4):
+        s = {"x": generate.normal((B, L, dm), 9700 + 8 * i, "f32").to(dev),
+             "w": [generate.normal((dm, dm), 9701 + 8 * i + j, "f32", std=dm ** -0.5).to(dev)
+                   for j in range(4)],
+             "g": torch.ones(dm, device=dev), "b": torch.zeros(dm, device=dev)}
+        s["q"], s["k"], s["v"] = (torch.empty((B, L, h, dm // h), device=dev) for _ in range(3))
+        s["y"] = torch.empty((B, L, dm), device=dev)
+        sets.append(s)
+    entry("project_qkv", "X [64, 128, 512] fp32 -> Q, K, V (h = 8)",
+          lambda s: mha.mha_project_qkv(s["x"], s["x"], *s["w"][:3], h, out=(s["q"], s["k"], s["v"])),
+          sets, 3 * 2.0 * M * dm * dm)
+    entry("out_proj", "O [64, 128, 8, 64] fp32 -> Y [64, 128, 512]",
+          lambda s: mha.mha_out_proj(s["q"], s["w"][3], out=s["y"]), sets, 2.0 * M * dm * dm)
+    entry("out_proj_post_norm", "LayerNorm(x + O W^O), [64, 128, 512] fp32",
+          lambda s: mha.mha_out_proj_post_norm(s["q"], s["w"][3], s["x"], s["g"], s["b"],
+                                               out=s["y"]), sets, 2.0 * M * dm * dm)
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -835,6 +895,7 @@ def main():
         heads = attention_sweep(dev, args.steps, args.warmup, configs.head_sizes())
         windowed = attention_sweep(dev, args.steps, args.warmup, configs.windows())
         decoded = decode_sweep(dev, args.steps, args.warmup, copy["gbps"])
+    f32 = fp32_path(dev, args.steps, args.warmup)
     cpu = oracle_cfg = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -870,6 +931,7 @@ def main():
         "head_size_sweep": heads,
         "window_sweep": windowed,
         "decode_sweep": decoded,
+        "fp32_path": f32,
         "cpu_baseline": cpu,
         "oracle_per_config": oracle_cfg,
     }
