@@ -56,3 +56,26 @@ def test_long_ragged_rows(case):
             for b in range(B):
                 if int(lens[b]) <= 0:
                     assert torch.equal(o[b].cpu(), torch.zeros_like(o[b].cpu()))
+
+
+def test_long_causal_first_row_and_prefix():
+    """Causal rows past 2048 queries (256-query workgroups, two query blocks
+    per wave): output row 0 is value row 0 bit-exactly (one legal key), and
+    rows up to t stay bit-identical when every key and value after t is
+    replaced (by values 50 times larger, so that the later rows of those
+    waves overflow their first reference and take the recomputation)."""
+    dev = device()
+    B, h, L, d = 1, 2, 2304, 64
+    q = generate.normal((B, L, h, d), 9400, "bf16")
+    k = generate.normal((B, L, h, d), 9401, "bf16")
+    v = generate.normal((B, L, h, d), 9402, "bf16")
+    say(f"case long causal prefix B={B} h={h} L={L}")
+    base = mha.mha_forward(q.to(dev), k.to(dev), v.to(dev), mask=CAUSAL).cpu()
+    assert torch.equal(base[:, 0], v[:, 0])
+    for t in (31, 255, 256, 1000, 2100):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, t + 1:] = generate.normal(k2[:, t + 1:].shape, 9410 + t, "bf16") * 50
+        v2[:, t + 1:] = generate.normal(v2[:, t + 1:].shape, 9420 + t, "bf16") * 50
+        o2 = mha.mha_forward(q.to(dev), k2.to(dev), v2.to(dev), mask=CAUSAL).cpu()
+        assert torch.equal(o2[:, :t + 1], base[:, :t + 1]), t
+        assert torch.isfinite(o2.float()).all(), t
