@@ -190,7 +190,7 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
  * Architecture").  The pages name the normalisation without its formula;
  * this is the usual per-feature-vector form, eps inside the square root.
  * One kernel: the product, the residual add and the statistics stay in fp32
- * on chip; only y (bf16) is written.
+ * on chip; only y (in the element type dt) is written.
  *
  *   o      [B, Lq, h, d_v] = [B*Lq, h*d_v]   the attention output (BLHD)
  *   w_o    [h*d_v, d_model]
@@ -204,8 +204,9 @@ int mha_out_proj(mha_dtype dt, int B, int Lq, int h, int d_v, int d_model,
  *
  * All pointers device, 16-byte aligned.  Supported: d_model in
  * {256, 512, 1024} and B*Lq, h*d_v < 2^31; MHA_BF16 also needs h*d_v % 32 ==
- * 0 and h*d_v * d_model < 2^30 (one kernel on MFMA); MHA_F32 (exact fp32
- * FMAs, the accuracy path) takes any h*d_v.  MHA_ERR_UNSUPPORTED otherwise;
+ * 0 and h*d_v * d_model < 2^30 (one kernel on MFMA); MHA_F32 (fp32
+ * products and accumulation on MFMA, the accuracy path) takes any h*d_v.
+ * MHA_ERR_UNSUPPORTED otherwise;
  * MHA_ERR_INVALID_ARG for negative sizes, a NaN, negative or infinite eps,
  * a NULL or misaligned pointer, or y partly overlapping x_res.  B*Lq == 0
  * is a no-op.
