@@ -262,7 +262,8 @@ __global__ __launch_bounds__(256, NT <= 4 ? 4 : 2) void attn_short_bf16_d64(
 // Workgroup = 4 waves = one (batch row, head, block of 128 queries); wave w
 // owns 32 consecutive queries, one per lane column.  K/V tiles of 32 rows
 // are staged in LDS as fp32 (rows at or past the length as zeros, so no
-// value stored there can reach the output).  Per tile a wave computes
+// value stored there can reach the output), loaded into registers one tile
+// ahead.  Per tile a wave computes
 //   S^T = K Q^T      D/2 MFMAs: lane (i, h = lane / 32) feeds K[key i][d]
 //                    and Q[query i][d] for d = h D/2 + s at step s
 //   scale, mask, online softmax with a running maximum (the partial output
@@ -350,20 +351,40 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_f32(const float* __restrict_
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
     float m_run = -INFINITY, l_part = 0.0f;
 
-    for (int t = t_first; t < n_tiles; ++t) {
-        __syncthreads();  // every wave is done with the previous tile
-        for (int idx = tid; idx < F32_KT * C4; idx += 256) {
+    // Tile t's K and V rows reach registers one tile ahead (thread tid
+    // takes chunks tid, tid + 256, ... of 4 floats: row chunk / (d/4)) and
+    // LDS between two barriers.
+    constexpr int NPF = (F32_KT * C4 + 255) / 256;
+    float4 kpre[NPF], vpre[NPF];
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) {
+            const int idx = tid + 256 * u;
             const int row = idx / C4, c = idx % C4;
             const int key = t * F32_KT + row;
             float4 kx = {0.0f, 0.0f, 0.0f, 0.0f}, vx = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (key < kv_end) {
+            if (idx < F32_KT * C4 && key < kv_end) {
                 kx = *(const float4*)(kp + (size_t)key * rs + 4 * c);
                 vx = *(const float4*)(vp + (size_t)key * rs + 4 * c);
             }
-            *(float4*)(sK + row * PITCH + 4 * c) = kx;
-            *(float4*)(sV + row * PITCH + 4 * c) = vx;
+            kpre[u] = kx;
+            vpre[u] = vx;
+        }
+    };
+    if (t_first < n_tiles) fetch(t_first);
+    for (int t = t_first; t < n_tiles; ++t) {
+        __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) {
+            const int idx = tid + 256 * u;
+            if (idx < F32_KT * C4) {
+                const int row = idx / C4, c = idx % C4;
+                *(float4*)(sK + row * PITCH + 4 * c) = kpre[u];
+                *(float4*)(sV + row * PITCH + 4 * c) = vpre[u];
+            }
         }
         __syncthreads();
+        if (t + 1 < n_tiles) fetch(t + 1);
         if (t < w_first || t >= n_mine) continue;  // wave-uniform
 
         // S^T = K Q^T: lane (i, h) holds key t*32 + (r % 4) + 8 (r / 4) + 4h
