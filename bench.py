@@ -354,13 +354,30 @@ def attention_sweep(dev, steps, warmup, workloads=None):
                                            w.window)
         tf = flops / sec / 1e12
         exps = accounting.legal_pairs(w.B, w.h, w.Lq, w.Lk, w.mask, inp["kv_lens"], w.window)
+        # The roofline of the row: Q, K, V and O cross HBM once, so FLOP per
+        # byte is 4 d (legal pairs) / bytes.  Under the ridge point
+        # (2.5e15 / 8e12 = 312) the attainable rate is that times 8 TB/s:
+        # the causal L = 1024 rows and the restricted-attention band are
+        # HBM-bound by it, the other rows MFMA-bound.
+        nbytes = accounting.attention_bytes(w.B, w.h, w.Lq, w.Lk, w.d, w.mask, inp["kv_lens"],
+                                            w.dtype)
+        intensity = flops / nbytes
+        attainable = min(PEAK_BF16_FLOPS, intensity * PEAK_HBM_BYTES)
+        gbps = nbytes / sec / 1e9
         out.append({"workload": w.name, "B": w.B, "h": w.h, "d": w.d, "L": w.Lq,
                     "window": w.window, "exps": exps, "flops": flops,
                     "mask": "causal" if w.mask & 2 else "none", "us": round(sec * 1e6, 2),
                     "host_us": round(host["s_per_step"] * 1e6, 2), "calls": host["calls"],
-                    "tflops": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)})
+                    "tflops": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16_FLOPS, 4),
+                    "bytes": nbytes, "gbps": round(gbps, 1),
+                    "frac_peak_hbm": round(gbps * 1e9 / PEAK_HBM_BYTES, 4),
+                    "flop_per_byte": round(intensity, 1),
+                    "roofline_bound": "mfma" if attainable >= PEAK_BF16_FLOPS else "hbm",
+                    "attainable_tflops": round(attainable / 1e12, 1),
+                    "frac_roofline": round(tf * 1e12 / attainable, 4)})
         log(f"  sweep {w.name}: {sec * 1e6:.1f} us, {tf:.1f} TFLOP/s "
-            f"({100 * tf * 1e12 / PEAK_BF16_FLOPS:.1f}% of bf16 peak)")
+            f"({100 * tf * 1e12 / PEAK_BF16_FLOPS:.1f}% of bf16 peak, "
+            f"{100 * tf * 1e12 / attainable:.1f}% of its roofline)")
         del sets
         torch.cuda.empty_cache()
     return out
