@@ -138,6 +138,11 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     // XCD x gets the (batch row, head) pairs x*nbh/8 .. (x+1)*nbh/8 - 1
     // whole, so every query block of a pair shares that XCD's L2 for its
     // K/V.  Causal: within each XCD the longest query blocks start first.
+    // A causal band keeps the pair-major order: its workgroups carry about
+    // equal work, and neighbouring query blocks, which share most of their
+    // keys, then run together while those keys are in L2 (longest-first
+    // spreads a pair's blocks over the whole launch, and K/V is fetched
+    // again from HBM).
     constexpr int SQB = QB;                // 32-query blocks per wave
     constexpr int SWQ = 32 * SQB;          // queries per wave
     constexpr int SBM = SWQ * SNW;         // queries per workgroup
@@ -162,14 +167,14 @@ __global__ __launch_bounds__(64 * SNW, (stream_occupancy<D, QB>())) void attn_st
     int bh, qt;
     if ((nbh & 7) == 0) {
         const int x = w & 7, slot = w >> 3, per = nbh >> 3;
-        if (CAUSAL) {
+        if (CAUSAL && !WIN) {
             qt = n_qtiles - 1 - slot / per;
             bh = x * per + slot % per;
         } else {
             bh = x * per + slot / n_qtiles;
             qt = slot % n_qtiles;
         }
-    } else if (CAUSAL) {
+    } else if (CAUSAL && !WIN) {
         qt = n_qtiles - 1 - w / nbh;
         bh = w % nbh;
     } else {
